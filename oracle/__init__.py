@@ -1,0 +1,188 @@
+"""CPU fp64 oracle for exact attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never calls it, and
+it shares no code with it.  The arithmetic lives in ``oracle.c`` (plain
+double-precision C, see that file's header for the definitions and the
+passages they follow); this module only marshals numpy arrays through ctypes.
+
+Every function takes a batch of G independent heads, arrays of shape
+[G, rows, d] in float64 (anything else is converted), and returns float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_P = ctypes.POINTER(ctypes.c_double)
+_PI = ctypes.POINTER(ctypes.c_int64)
+_I = ctypes.c_int64
+
+
+GCC_FLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-shared", "-fPIC"]
+
+
+def compile_source(src: str, out: str) -> str:
+    """Compile one C source of the oracle into a shared library at ``out``."""
+    tmp = out + ".tmp%d" % os.getpid()
+    subprocess.run(["gcc", *GCC_FLAGS, "-o", tmp, src, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (-O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        compile_source(_SRC, _LIB)
+    return _LIB
+
+
+class OracleLib:
+    """ctypes binding of one compiled copy of oracle.c."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        lib.oracle_attn_fwd.argtypes = [_I, _I, _I, _I, _P, _P, _P, _PI, ctypes.c_int,
+                                        ctypes.c_double, _P, _P]
+        lib.oracle_attn_fwd.restype = ctypes.c_int
+        lib.oracle_attn_fwd_online.argtypes = [_I, _I, _I, _I, _P, _P, _P, _PI, ctypes.c_int,
+                                               ctypes.c_double, _I, _P, _P]
+        lib.oracle_attn_fwd_online.restype = ctypes.c_int
+        lib.oracle_attn_bwd.argtypes = [_I, _I, _I, _P, _P, _P, _P, ctypes.c_int, ctypes.c_double,
+                                        _PI, _I, _P, _PI, _I, _P, _P]
+        lib.oracle_attn_bwd.restype = ctypes.c_int
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+    def num_threads(self) -> int:
+        return int(self.lib.oracle_num_threads())
+
+    def fwd(self, q, k, v, causal: bool, scale: float, qpos=None):
+        """Three-pass forward.  Returns (o [G,nq,d], lse [G,nq]).
+
+        qpos gives the sequence position of each query row (default 0..nq-1);
+        with causal=True key j is visible to row i iff j <= qpos[i].
+        """
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        G, nq, d = q.shape
+        nk = k.shape[1]
+        if k.shape != (G, nk, d) or v.shape != (G, nk, d):
+            raise ValueError("shape mismatch")
+        qpos = np.ascontiguousarray(np.arange(nq) if qpos is None else qpos, dtype=np.int64)
+        if qpos.shape != (nq,):
+            raise ValueError("qpos must have one entry per query row")
+        o = np.empty((G, nq, d), np.float64)
+        lse = np.empty((G, nq), np.float64)
+        rc = self.lib.oracle_attn_fwd(G, nq, nk, d, _ptr(q), _ptr(k), _ptr(v), _iptr(qpos),
+                                      int(bool(causal)), float(scale), _ptr(o), _ptr(lse))
+        if rc != 0:
+            raise MemoryError("oracle_attn_fwd failed (%d)" % rc)
+        return o, lse
+
+    def fwd_online(self, q, k, v, causal: bool, scale: float, block: int, qpos=None):
+        """Block-wise running-max forward (the validator).  Returns (o, lse)."""
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        G, nq, d = q.shape
+        nk = k.shape[1]
+        qpos = np.ascontiguousarray(np.arange(nq) if qpos is None else qpos, dtype=np.int64)
+        o = np.empty((G, nq, d), np.float64)
+        lse = np.empty((G, nq), np.float64)
+        rc = self.lib.oracle_attn_fwd_online(G, nq, nk, d, _ptr(q), _ptr(k), _ptr(v), _iptr(qpos),
+                                             int(bool(causal)), float(scale), int(block),
+                                             _ptr(o), _ptr(lse))
+        if rc != 0:
+            raise RuntimeError("oracle_attn_fwd_online failed (%d)" % rc)
+        return o, lse
+
+    def bwd(self, q, k, v, dout, causal: bool, scale: float, rows=None, keys=None):
+        """Analytic backward.  Returns (dq, dk, dv).
+
+        rows / keys select which query rows of dq and which key rows of dk, dv
+        are computed (default: all).  dq has shape [G, len(rows), d]; dk, dv
+        [G, len(keys), d].  An empty selection computes nothing for that output.
+        """
+        q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+        G, n, d = q.shape
+        for a in (k, v, dout):
+            if a.shape != (G, n, d):
+                raise ValueError("shape mismatch")
+        rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
+        keys_a = None if keys is None else np.ascontiguousarray(keys, dtype=np.int64).reshape(-1)
+        nrows = n if rows_a is None else len(rows_a)
+        nkeys = n if keys_a is None else len(keys_a)
+        for sel in (rows_a, keys_a):
+            if sel is not None and len(sel) and (sel.min() < 0 or sel.max() >= n):
+                raise IndexError("row/key index out of range")
+        dq = np.empty((G, nrows, d), np.float64)
+        dk = np.empty((G, nkeys, d), np.float64)
+        dv = np.empty((G, nkeys, d), np.float64)
+        pad = np.zeros(1, np.int64)  # a valid pointer for an empty selection
+        rp = None if rows_a is None else (rows_a if nrows else pad)
+        kp = None if keys_a is None else (keys_a if nkeys else pad)
+        rc = self.lib.oracle_attn_bwd(G, n, d, _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                                      int(bool(causal)), float(scale),
+                                      _iptr(rp), nrows, _ptr(dq), _iptr(kp), nkeys,
+                                      _ptr(dk), _ptr(dv))
+        if rc != 0:
+            raise MemoryError("oracle_attn_bwd failed (%d)" % rc)
+        return dq, dk, dv
+
+
+def _load() -> OracleLib:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        _lib = OracleLib(_LIB)
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    if a.ndim == 2:
+        a = a[None]
+    if a.ndim != 3:
+        raise ValueError("expected [G, rows, d] or [rows, d], got shape %r" % (a.shape,))
+    return a
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_P)
+
+
+def _iptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(_PI)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return _load().num_threads()
+
+
+def fwd(q, k, v, causal: bool, scale: float, qpos=None):
+    return _load().fwd(q, k, v, causal, scale, qpos)
+
+
+def fwd_online(q, k, v, causal: bool, scale: float, block: int, qpos=None):
+    return _load().fwd_online(q, k, v, causal, scale, block, qpos)
+
+
+def bwd(q, k, v, dout, causal: bool, scale: float, rows=None, keys=None):
+    return _load().bwd(q, k, v, dout, causal, scale, rows, keys)
+
+
+fwd.__doc__ = OracleLib.fwd.__doc__
+fwd_online.__doc__ = OracleLib.fwd_online.__doc__
+bwd.__doc__ = OracleLib.bwd.__doc__
