@@ -1,0 +1,142 @@
+"""ctypes binding of the C ABI in include/attn.h (argument marshalling only).
+
+``attn_fwd``, ``attn_bwd``, ``attn_bwd_workspace_bytes`` and
+``attn_status_string`` call the C functions of the same names with raw
+integers (device pointers, sizes, a hipStream_t).  ``fwd`` and ``bwd`` are
+conveniences for torch tensors: they allocate the outputs (and the backward
+workspace) with torch and pass ``data_ptr()`` values and the current stream.
+Every step of the computation runs in the HIP library; if the library is not
+built, the first call raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libattn.so")
+
+ATTN_F16, ATTN_BF16 = 0, 1
+STATUS = {
+    0: "ATTN_OK", 1: "ATTN_E_NULL", 2: "ATTN_E_SHAPE", 3: "ATTN_E_UNSUPPORTED",
+    4: "ATTN_E_ALIGN", 5: "ATTN_E_ALIAS", 6: "ATTN_E_WORKSPACE", 7: "ATTN_E_HIP",
+}
+EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_string")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("%s (%d): %s" % (STATUS.get(status, "?"), status, msg))
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Open libattn.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("HIP library %s is missing: build it first "
+                               "(python -m io_aware_exact_06_amd.build)" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+        L.attn_fwd.restype = i
+        L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i]
+        L.attn_bwd_workspace_bytes.restype = sz
+        L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+        L.attn_bwd.restype = i
+        L.attn_status_string.argtypes = [i]
+        L.attn_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+# ---- the C functions, same names, raw arguments --------------------------------
+
+def attn_status_string(status: int) -> str:
+    return lib().attn_status_string(int(status)).decode()
+
+
+def attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, stream) -> int:
+    return lib().attn_fwd(q, k, v, o, lse, B, H, N, d, int(causal), float(scale), dtype, stream)
+
+
+def attn_bwd_workspace_bytes(B, H, N, d) -> int:
+    return int(lib().attn_bwd_workspace_bytes(B, H, N, d))
+
+
+def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal, scale, dtype,
+             workspace, workspace_bytes, stream) -> int:
+    return lib().attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, int(causal),
+                          float(scale), dtype, workspace, workspace_bytes, stream)
+
+
+def _check(status: int):
+    if status != 0:
+        raise AttnError(status, attn_status_string(status))
+
+
+# ---- torch conveniences ---------------------------------------------------------
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float16:
+        return ATTN_F16
+    raise TypeError("q/k/v must be float16 or bfloat16, got %s" % t.dtype)
+
+
+def _stream_handle(device):
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _shape(q, *others):
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    for t in others:
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("all tensors must share shape, dtype and device")
+    for t in (q, *others):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    return tuple(int(x) for x in q.shape)
+
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, o=None, lse=None):
+    """O, lse = attention(q, k, v) on q's device and current stream."""
+    import torch
+    B, H, N, d = _shape(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check(attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                    B, H, N, d, causal, scale, _dtype_code(q), _stream_handle(q.device)))
+    return o, lse
+
+
+def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
+        dq=None, dk=None, dv=None, workspace=None):
+    """dq, dk, dv of attention by recomputation, on q's device and current stream."""
+    import torch
+    B, H, N, d = _shape(q, k, v, o, dout)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    need = attn_bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                    lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
+                    causal, scale, _dtype_code(q), workspace.data_ptr(), workspace.numel(),
+                    _stream_handle(q.device)))
+    return dq, dk, dv

@@ -1,0 +1,96 @@
+"""The C-ABI library: it loads, exports every function its header declares,
+and rejects bad arguments on the host, before any GPU work (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from io_aware_exact_06_amd import attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(attn.EXPORTS)
+    L = attn.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for s in range(8):
+        assert attn.attn_status_string(s) and attn.attn_status_string(s) != "unknown status"
+    assert attn.attn_status_string(99) == "unknown status"
+
+
+# Fake device addresses: validation never dereferences them.
+A = 0x10000000
+SZ = 1 * 2 * 64 * 64 * 2  # bytes of a [1,2,64,64] 16-bit tensor
+
+
+def fwd(q=A, k=A + 0x100000, v=A + 0x200000, o=A + 0x300000, lse=A + 0x400000, B=1, H=2, N=64, d=64,
+        causal=0, scale=0.125, dtype=1):
+    return attn.attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, None)
+
+
+def bwd(ws_bytes=None, ws=A + 0x900000, **kw):
+    a = dict(q=A, k=A + 0x100000, v=A + 0x200000, o=A + 0x300000, dout=A + 0x400000, lse=A + 0x500000,
+             dq=A + 0x600000, dk=A + 0x700000, dv=A + 0x800000, B=1, H=2, N=64, d=64, causal=0,
+             scale=0.125, dtype=1)
+    a.update(kw)
+    if ws_bytes is None:
+        ws_bytes = attn.attn_bwd_workspace_bytes(a["B"], a["H"], a["N"], a["d"])
+    return attn.attn_bwd(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"],
+                         a["B"], a["H"], a["N"], a["d"], a["causal"], a["scale"], a["dtype"], ws, ws_bytes,
+                         None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), 1), (dict(o=0), 1), (dict(lse=0), 1),
+    (dict(N=-1), 2), (dict(B=-3), 2),
+    (dict(d=96), 3), (dict(d=32), 3), (dict(dtype=2), 3), (dict(causal=2), 3),
+    (dict(scale=float("nan")), 3), (dict(scale=float("inf")), 3), (dict(scale=-1.0), 3),
+    (dict(q=A + 8), 4), (dict(o=A + 0x300002), 4), (dict(lse=A + 0x400002), 4),
+    (dict(o=A + 0x100), 5), (dict(lse=A + 0x300000 + SZ - 4), 5), (dict(o=A + 0x200000), 5),
+    (dict(B=1 << 30, H=1 << 30, N=1 << 20), 2),
+])
+def test_fwd_rejects(kw, status):
+    assert fwd(**kw) == status
+
+
+def test_fwd_empty_problem_is_a_no_op():
+    # nothing is enqueued and the pointers are not examined
+    assert fwd(q=0, k=0, v=0, o=0, lse=0, N=0) == 0
+    assert fwd(q=0, k=0, v=0, o=0, lse=0, B=0) == 0
+
+
+def test_bwd_workspace_bytes():
+    B, H, N, d = 2, 3, 100, 128
+    n = attn.attn_bwd_workspace_bytes(B, H, N, d)
+    assert n >= B * H * N * (d + 1) * 4
+    assert attn.attn_bwd_workspace_bytes(0, 3, 100, 128) == 0
+    assert attn.attn_bwd_workspace_bytes(-1, 3, 100, 128) == ctypes.c_size_t(-1).value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dout=0), 1), (dict(dv=0), 1), (dict(ws=0), 6),
+    (dict(ws_bytes=100), 6), (dict(d=80), 3),
+    (dict(dq=A + 4), 4), (dict(ws=A + 0x900008), 4),
+    (dict(dq=A + 0x400000), 5), (dict(dk=A + 0x600000), 5), (dict(dv=A + 0x500000), 5),
+    (dict(ws=A + 0x800000), 6), (dict(ws=A + 0x100000), 6),
+])
+def test_bwd_rejects(kw, status):
+    assert bwd(**kw) == status
+
+
+def test_bwd_empty_problem_is_a_no_op():
+    assert bwd(q=0, k=0, v=0, o=0, dout=0, lse=0, dq=0, dk=0, dv=0, ws=0, ws_bytes=0, N=0) == 0
