@@ -1,0 +1,171 @@
+"""Benchmark of the fused exact-attention path on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+the forward (O and lse) and the recompute backward (dQ, dK, dV) of
+B=1, H=32, N=8192, d=128, causal, bf16 attention with inputs resident in HBM.
+
+    python bench.py [--steps K] [--warmup W] [--passes fwd|fwdbwd] [--no-cpu-baseline]
+
+Prints one JSON line.  Throughput is algorithmic FLOP/s: forward
+4*d*pairs, backward 10*d*pairs (five d-deep products per unmasked pair,
+the score recomputation included), pairs = N(N+1)/2 per head when causal.
+Kernel durations come from HIP events recorded on the stream the library
+launches on (torch's current stream).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense 16-bit MFMA FLOP/clk/CU
+WORKLOAD_INDEX = 3         # B=1 H=32 N=8192 d=128 bf16 causal, forward + backward
+METRIC = "fused attention fwd/bwd TFLOP/s and % MFMA peak, N=8192 d=128 causal bf16"
+
+
+def flops(w, passes):
+    pairs = w.pairs_per_head() * w.B * w.H
+    f = 4.0 * w.d * pairs
+    b = 10.0 * w.d * pairs
+    return f, (b if "bwd" in passes else 0.0)
+
+
+def cpu_baseline(w, inp, scale, passes):
+    """The fp64 oracle on the host's cores, on one head of the workload."""
+    import numpy as np
+
+    import oracle
+    q, k, v = (inp[n][0, 0].double().numpy()[None] for n in ("q", "k", "v"))
+    pairs = w.pairs_per_head()
+    t0 = time.perf_counter()
+    oracle.fwd(q, k, v, w.causal, scale)
+    t_f = time.perf_counter() - t0
+    fl = 4.0 * w.d * pairs
+    t = t_f
+    sample = "head (b=0,h=0) of the workload, forward"
+    if "bwd" in passes and t_f < 15.0:
+        do = inp["dout"][0, 0].double().numpy()[None]
+        t0 = time.perf_counter()
+        oracle.bwd(q, k, v, do, w.causal, scale)
+        t += time.perf_counter() - t0
+        fl += 10.0 * w.d * pairs
+        sample = "head (b=0,h=0) of the workload, forward + backward"
+    return {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": sample + " (N=%d, d=%d, causal), %.1f s" % (w.N, w.d, t),
+            "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--passes", choices=["fwd", "fwdbwd"], default="fwdbwd")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build runs on a single MI355X; "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from io_aware_exact_06_amd import attn
+    from io_aware_exact_06_amd.inputs import WORKLOADS, default_scale, workload_inputs
+
+    if not os.path.exists(attn.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+
+    w = WORKLOADS[WORKLOAD_INDEX]
+    scale = default_scale(w.d)
+    inp = workload_inputs(WORKLOAD_INDEX)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "dout"))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(max(1, attn.attn_bwd_workspace_bytes(w.B, w.H, w.N, w.d)), dtype=torch.uint8, device=dev)
+    bwd = "bwd" in args.passes
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        attn.fwd(q, k, v, w.causal, scale, o=o, lse=lse)
+        if ev is not None:
+            ev[1].record()
+        if bwd:
+            attn.bwd(q, k, v, o, do, lse, w.causal, scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+            if ev is not None:
+                ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    fwd_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    bwd_ms = sorted(e[1].elapsed_time(e[2]) for e in evs) if bwd else [0.0]
+    med = lambda a: a[len(a) // 2]
+    finite = bool(torch.isfinite(o).all() and torch.isfinite(lse).all())
+    if bwd:
+        finite = finite and bool(torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all())
+    ff, fb = flops(w, args.passes)
+    ms_step = wall * 1e3 / args.steps
+    f_tf = ff / (sum(fwd_ms) / len(fwd_ms) * 1e-3) / 1e12
+    b_tf = fb / (sum(bwd_ms) / len(bwd_ms) * 1e-3) / 1e12 if bwd else None
+    value = (ff + fb) / (ms_step * 1e-3) / 1e12
+    # Dominant kernel: the backward pass when it runs, else the forward.
+    if bwd:
+        dom = {"kernel": "attn_bwd (dK/dV/dQ main kernel + D and dQ-convert passes)",
+               "achieved": b_tf, "avg_ms": sum(bwd_ms) / len(bwd_ms)}
+    else:
+        dom = {"kernel": "attn_fwd_kernel", "achieved": f_tf, "avg_ms": sum(fwd_ms) / len(fwd_ms)}
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: iid N(0,1) fp32 rounded to bf16, seed 1003",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "dtype": w.dtype, "passes": args.passes},
+        "fwd": {"median_ms": round(med(fwd_ms), 4), "min_ms": round(fwd_ms[0], 4),
+                "tflops": round(f_tf, 2), "pct_peak": round(100 * f_tf / PEAK_BF16_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(dom["achieved"], 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(dom["achieved"] / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": dom["kernel"], "avg_ms": round(dom["avg_ms"], 4)},
+        "outputs_finite": finite,
+    }
+    if bwd:
+        out["bwd"] = {"median_ms": round(med(bwd_ms), 4), "min_ms": round(bwd_ms[0], 4),
+                      "tflops": round(b_tf, 2), "pct_peak": round(100 * b_tf / PEAK_BF16_TFLOPS, 2)}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp, scale, args.passes)
+    print(json.dumps(out), flush=True)
+    if not finite:
+        sys.exit(1)
+
+
+if __name__ == "__main__":
+    main()

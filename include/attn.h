@@ -41,8 +41,7 @@
  * rejected call returns a nonzero status and has no side effect.  A failed
  * kernel launch returns ATTN_E_HIP.  Faults during execution surface at the
  * caller's next synchronisation, as for any HIP work.  The functions are
- * reentrant.  The forward is bitwise deterministic; the backward's dQ is
- * accumulated with fp32 atomics and may differ in the last bits between runs.
+ * reentrant.  Both passes are bitwise deterministic (no atomics).
  */
 #ifndef IO_AWARE_EXACT_ATTN_H
 #define IO_AWARE_EXACT_ATTN_H
@@ -78,9 +77,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * Bytes of device workspace attn_bwd needs for these sizes (0 for an empty
- * problem): an fp32 dQ accumulator [B, H, N, d] and the fp32 row terms
- * D_i = <dO_i, O_i> [B, H, N], each region 256-byte aligned.  Returns
- * (size_t)-1 for negative sizes.
+ * problem): the fp32 row terms D_i = <dO_i, O_i>, [B, H, N], rounded up to a
+ * multiple of 256 bytes.  Returns (size_t)-1 for negative sizes.
  */
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
 

@@ -83,7 +83,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d) {
     if (B < 0 || H < 0 || N < 0 || d < 0) return (size_t)-1;
     if ((int64_t)B * H * N == 0) return 0;
-    return attn::bwd_workspace_layout(B, H, N, d).total;
+    (void)d;
+    return attn::bwd_workspace_bytes(B, H, N);
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -99,22 +100,20 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     for (const void* p : a16)
         if (!aligned(p, 16)) return ATTN_E_ALIGN;
     if (!aligned(lse, 4)) return ATTN_E_ALIGN;
-    const attn::BwdWorkspaceLayout wl = attn::bwd_workspace_layout(B, H, N, d);
-    if (workspace_bytes < wl.total) return ATTN_E_WORKSPACE;
+    const size_t ws_need = attn::bwd_workspace_bytes(B, H, N);
+    if (workspace_bytes < ws_need) return ATTN_E_WORKSPACE;
     const size_t tb = (size_t)elems * 2, lb = (size_t)rows * 4;
     const Range ins[] = {range_of(q, tb), range_of(k, tb), range_of(v, tb), range_of(o, tb),
                          range_of(dout, tb), range_of(lse, lb)};
     const Range outs[] = {range_of(dq, tb), range_of(dk, tb), range_of(dv, tb),
-                          range_of(workspace, wl.total)};
+                          range_of(workspace, ws_need)};
     for (int i = 0; i < 4; ++i) {
         for (const Range& r : ins)
             if (overlap(outs[i], r)) return i == 3 ? ATTN_E_WORKSPACE : ATTN_E_ALIAS;
         for (int j = i + 1; j < 4; ++j)
             if (overlap(outs[i], outs[j])) return j == 3 ? ATTN_E_WORKSPACE : ATTN_E_ALIAS;
     }
-    char* ws = (char*)workspace;
-    attn::BwdParams p{q, k, v, o, dout, lse, dq, dk, dv,
-                      (float*)(ws + wl.dq_acc_offset), (float*)(ws + wl.delta_offset),
+    attn::BwdParams p{q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace,
                       B, H, N, d, causal, dtype, scale, stream};
     return attn::launch_bwd(p) == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }

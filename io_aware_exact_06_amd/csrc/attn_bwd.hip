@@ -1,8 +1,408 @@
-// attn_bwd.hip -- recompute backward (placeholder until the kernels land).
+// attn_bwd.hip -- recompute backward of fused exact attention for gfx950.
+//
+// Only O and the per-row lse were kept by the forward; the score tiles are
+// rebuilt here from Q, K and lse (the hotdry blog's section "4. 重计算
+// （Recomputation）策略": store one statistic per row, recompute the QK^T
+// blocks in the backward pass, stream the gradients).  With
+// P = exp(scale * Q K^T - lse) (zero where masked) and D_i = <dO_i, O_i>:
+//
+//     dV = P^T dO,   dS = P o (dO V^T - D),   dQ = scale * dS K,   dK = scale * dS^T Q.
+//
+// Two kernels, neither with atomics (fp32 global atomics run at ~1.3 TB/s on
+// this part, far too slow for per-tile dQ partial sums):
+//
+//   attn_bwd_dq_kernel    query-tile stationary.  Computes D for its rows
+//                         (written to the workspace), then streams K and V
+//                         tiles: S^T = K Q^T, dP^T = V dO^T, dS^T, and
+//                         dQ^T += K^T dS^T.  Same orientation as the forward:
+//                         lane l owns query l % 32, so lse and D are per-lane
+//                         scalars.
+//   attn_bwd_dkdv_kernel  key-tile stationary, launched second (it reads D).
+//                         K and V of its 128 keys stay in registers; it
+//                         streams Q and dO tiles: S = Q K^T, dP = dO V^T,
+//                         dV^T += dO^T P, dK^T += Q^T dS.  Here lane l owns
+//                         key l % 32, so P and dS leave their accumulators
+//                         directly as B operands.
+//
+// The second kernel recomputes S and dP, so the backward performs seven
+// d-deep products per unmasked pair instead of five; it buys freedom from
+// atomics and a deterministic result.
+
+#include "attn_device.h"
 #include "attn_launch.h"
 
 namespace attn {
 
-hipError_t launch_bwd(const BwdParams&) { return hipErrorNotSupported; }
+namespace {
+
+constexpr int kThreads = 256;
+constexpr float kPosInf = __builtin_inff();
+
+// 16-bit storage -> fp32.
+template <class T>
+__device__ inline float lo16(uint32_t u);
+template <class T>
+__device__ inline float hi16(uint32_t u);
+template <>
+__device__ inline float lo16<BF16>(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
+template <>
+__device__ inline float hi16<BF16>(uint32_t u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
+template <>
+__device__ inline float lo16<F16>(uint32_t u) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xffffu));
+}
+template <>
+__device__ inline float hi16<F16>(uint32_t u) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
+}
+
+template <class T>
+__device__ inline float dot8(const u32x4& a, const u32x4& b) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s += lo16<T>(a[i]) * lo16<T>(b[i]) + hi16<T>(a[i]) * hi16<T>(b[i]);
+    return s;
+}
+
+// Write a wave's 32 x D accumulator tile (lane l: column l % 32 of each 32-row
+// block db, rows 32*db + 8*(e/4) + 4*(l/32) + e%4), times `mul`, transposed
+// into row (row0 + l % 32) of a row-major LDS staging tile.
+template <class T, int D, int STR>
+__device__ inline void stage_transposed(uint16_t* st, int row, int h, const f32x16 (&acc)[D / 32], float mul) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            u32x2 pk = {pack2<T>(acc[db][4 * g] * mul, acc[db][4 * g + 1] * mul),
+                        pack2<T>(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul)};
+            *(u32x2*)(st + row * STR + 32 * db + 8 * g + 4 * h) = pk;
+        }
+}
+
+// Copy `rows` staged rows (row r of the tile -> global row r0 + r, if < N).
+template <int D, int STR>
+__device__ inline void store_staged(uint16_t* __restrict__ dst, const uint16_t* st, int rows, int r0, int N, int tid) {
+    constexpr int CH = D / 8;
+    for (int ch = tid; ch < rows * CH; ch += kThreads) {
+        const int r = ch / CH, col = ch % CH;
+        if (r0 + r < N) *(u32x4*)(dst + (int64_t)(r0 + r) * D + 8 * col) = *(const u32x4*)(st + r * STR + 8 * col);
+    }
+}
+
+// ============================================================================
+// dQ and D: one work group per (batch*head, 128 query rows), 4 waves x 32 rows.
+// ============================================================================
+constexpr int kQ_BQ = 128;
+constexpr int kQ_BK = 64;
+
+template <class T, int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 2)))
+void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                        const uint16_t* __restrict__ V, const uint16_t* __restrict__ O,
+                        const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
+                        float* __restrict__ Delta, uint16_t* __restrict__ dQ, int N, int ntq, float scale,
+                        float c) {
+    constexpr int STR = LdsStride<D>::value;
+    constexpr int KS = D / 16, DB = D / 32, KB = kQ_BK / 32;
+    constexpr int TILE = kQ_BK * STR;
+    static_assert(kQ_BQ * STR <= 2 * TILE, "staging must fit in the K buffers");
+    using Copy = TileCopy<kQ_BK, D, kThreads>;
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[2 * TILE];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int n32 = lane & 31, h = lane >> 5;
+    const int item = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int bh = item / ntq;
+    const int qt = CAUSAL ? ntq - 1 - item % ntq : item % ntq;
+    const int64_t base = (int64_t)bh * N * D;
+    const uint16_t *Qh = Q + base, *Kh = K + base, *Vh = V + base, *Oh = O + base, *dOh = dO + base;
+    const int q0 = qt * kQ_BQ;
+    const int wq0 = q0 + 32 * w;
+    const int qrow = wq0 + n32;
+    const bool valid = qrow < N;
+
+    // Resident Q^T and dO^T fragments; D = <dO, O> for this row.
+    u32x4 qf[KS], dof[KS];
+    float dpart = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const int64_t off = (int64_t)qrow * D + 16 * ks + 8 * h;
+        qf[ks] = valid ? *(const u32x4*)(Qh + off) : z;
+        dof[ks] = valid ? *(const u32x4*)(dOh + off) : z;
+        const u32x4 of = valid ? *(const u32x4*)(Oh + off) : z;
+        dpart += dot8<T>(dof[ks], of);
+    }
+    const float Dq = sum_with_other_half(dpart);
+    if (h == 0 && valid) Delta[(int64_t)bh * N + qrow] = Dq;
+    const float lse2 = valid ? LSE[(int64_t)bh * N + qrow] * kLog2e : kPosInf;
+
+    const int kend = CAUSAL ? min(N, q0 + kQ_BQ) : N;
+    const int nkt = (kend + kQ_BK - 1) / kQ_BK;
+    Copy kc, vc;
+    kc.load(Kh, 0, N, tid);
+    vc.load(Vh, 0, N, tid);
+    kc.store(Ks, tid);
+    vc.store(Vs, tid);
+    __syncthreads();
+
+    f32x16 dqacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dqacc[db][e] = 0.f;
+    const int tr_off = tr_lane_offset<STR>(lane);
+
+    for (int jt = 0; jt < nkt; ++jt) {
+        const int buf = (jt & 1) * TILE;
+        const int k0 = jt * kQ_BK;
+        const bool more = jt + 1 < nkt;
+        if (more) {
+            kc.load(Kh, k0 + kQ_BK, N, tid);
+            vc.load(Vh, k0 + kQ_BK, N, tid);
+        }
+        if (!CAUSAL || k0 <= wq0 + 31) {
+            f32x16 s[KB], dp[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    s[kb][e] = 0.f;
+                    dp[kb][e] = 0.f;
+                }
+                const int roff = buf + (kb * 32 + n32) * STR + 8 * h;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    s[kb] = mfma32<T>(*(const u32x4*)(Ks + roff + 16 * ks), qf[ks], s[kb]);
+                    dp[kb] = mfma32<T>(*(const u32x4*)(Vs + roff + 16 * ks), dof[ks], dp[kb]);
+                }
+            }
+            const bool masked = (k0 + kQ_BK > N) || (CAUSAL && k0 + kQ_BK - 1 > wq0);
+            u32x4 b[KB][2];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                f32x16 ds;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e], c, -lse2));
+                    if (masked) {
+                        const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+                        if (key >= N || (CAUSAL && key > qrow)) p = 0.f;
+                    }
+                    ds[e] = p * (dp[kb][e] - Dq);
+                }
+                pack_acc_as_b<T>(ds, b[kb][0], b[kb][1]);
+            }
+            const uint16_t* kt = Ks + buf + tr_off;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+                        dqacc[db] = mfma32<T>(tr_operand<STR>(kt, kb * 32 + 16 * t, 32 * db), b[kb][t], dqacc[db]);
+        }
+        if (more) {
+            kc.store(Ks + TILE - buf, tid);
+            vc.store(Vs + TILE - buf, tid);
+        }
+        __syncthreads();
+    }
+
+    stage_transposed<T, D, STR>(Ks, 32 * w + n32, h, dqacc, scale);
+    __syncthreads();
+    store_staged<D, STR>(dQ + base, Ks, kQ_BQ, q0, N, tid);
+}
+
+// ============================================================================
+// dK and dV: one work group per (batch*head, 128 key rows), 4 waves x 32 keys.
+// ============================================================================
+constexpr int kK_BK = 128;
+constexpr int kK_BQ = 64;
+
+template <class T, int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 2)))
+void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                          const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                          const float* __restrict__ LSE, const float* __restrict__ Delta,
+                          uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int ntk, float scale,
+                          float c) {
+    constexpr int STR = LdsStride<D>::value;
+    constexpr int KS = D / 16, DB = D / 32, QB = kK_BQ / 32;
+    constexpr int TILE = kK_BQ * STR;
+    static_assert(kK_BK * STR <= 2 * TILE, "staging must fit in the Q buffers");
+    using Copy = TileCopy<kK_BQ, D, kThreads>;
+    __shared__ __attribute__((aligned(16))) uint16_t Qs[2 * TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t dOs[2 * TILE];
+    __shared__ __attribute__((aligned(16))) float stats[2][2][kK_BQ];  // [buffer][lse*log2e, D][row]
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int n32 = lane & 31, h = lane >> 5;
+    const int item = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int bh = item / ntk;
+    const int kt = item % ntk;  // causal: low key tiles see the most queries and run first
+    const int64_t base = (int64_t)bh * N * D;
+    const uint16_t *Qh = Q + base, *Kh = K + base, *Vh = V + base, *dOh = dO + base;
+    const float* lseh = LSE + (int64_t)bh * N;
+    const float* Dh = Delta + (int64_t)bh * N;
+    const int k0 = kt * kK_BK;
+    const int wk0 = k0 + 32 * w;
+    const int krow = wk0 + n32;
+
+    // Resident K and V fragments (B operands of S = Q K^T and dP = dO V^T).
+    u32x4 kf[KS], vf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const int64_t off = (int64_t)krow * D + 16 * ks + 8 * h;
+        kf[ks] = krow < N ? *(const u32x4*)(Kh + off) : z;
+        vf[ks] = krow < N ? *(const u32x4*)(Vh + off) : z;
+    }
+
+    const int q_start = CAUSAL ? (k0 / kK_BQ) * kK_BQ : 0;
+    const int nqt = (N - q_start + kK_BQ - 1) / kK_BQ;
+    Copy qc, oc;
+    float st_l = kPosInf, st_d = 0.f;
+    auto load_stats = [&](int r0) {
+        if (tid < kK_BQ) {
+            const int r = r0 + tid;
+            st_l = r < N ? lseh[r] * kLog2e : kPosInf;  // rows past the end get P = 0
+            st_d = r < N ? Dh[r] : 0.f;
+        }
+    };
+    auto store_stats = [&](int b) {
+        if (tid < kK_BQ) {
+            stats[b][0][tid] = st_l;
+            stats[b][1][tid] = st_d;
+        }
+    };
+    qc.load(Qh, q_start, N, tid);
+    oc.load(dOh, q_start, N, tid);
+    load_stats(q_start);
+    qc.store(Qs, tid);
+    oc.store(dOs, tid);
+    store_stats(0);
+    __syncthreads();
+
+    f32x16 dkacc[DB], dvacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            dkacc[db][e] = 0.f;
+            dvacc[db][e] = 0.f;
+        }
+    const int tr_off = tr_lane_offset<STR>(lane);
+
+    for (int it = 0; it < nqt; ++it) {
+        const int sb = it & 1;
+        const int buf = sb * TILE;
+        const int qq0 = q_start + it * kK_BQ;
+        const bool more = it + 1 < nqt;
+        if (more) {
+            qc.load(Qh, qq0 + kK_BQ, N, tid);
+            oc.load(dOh, qq0 + kK_BQ, N, tid);
+            load_stats(qq0 + kK_BQ);
+        }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const int qb0 = qq0 + 32 * qb;  // first query row of this 32-row block
+            if (CAUSAL && qb0 + 31 < wk0) continue;  // every query precedes every key of this wave
+            f32x16 s, dp;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                s[e] = 0.f;
+                dp[e] = 0.f;
+            }
+            const int roff = buf + (32 * qb + n32) * STR + 8 * h;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                s = mfma32<T>(*(const u32x4*)(Qs + roff + 16 * ks), kf[ks], s);
+                dp = mfma32<T>(*(const u32x4*)(dOs + roff + 16 * ks), vf[ks], dp);
+            }
+            // Row statistics of the 16 query rows this lane holds: rows 8g + 4h + (0..3).
+            f32x16 ls, dd;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 l4 = *(const f32x4*)(&stats[sb][0][32 * qb + 8 * g + 4 * h]);
+                const f32x4 d4 = *(const f32x4*)(&stats[sb][1][32 * qb + 8 * g + 4 * h]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    ls[4 * g + i] = l4[i];
+                    dd[4 * g + i] = d4[i];
+                }
+            }
+            const bool masked = CAUSAL && qb0 < wk0 + 31;
+            f32x16 p, ds;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -ls[e]));
+                if (masked && qb0 + 8 * (e >> 2) + 4 * h + (e & 3) < krow) pe = 0.f;
+                p[e] = pe;
+                ds[e] = pe * (dp[e] - dd[e]);
+            }
+            u32x4 bp[2], bds[2];
+            pack_acc_as_b<T>(p, bp[0], bp[1]);
+            pack_acc_as_b<T>(ds, bds[0], bds[1]);
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    dvacc[db] = mfma32<T>(tr_operand<STR>(dOs + buf + tr_off, 32 * qb + 16 * t, 32 * db), bp[t], dvacc[db]);
+                    dkacc[db] = mfma32<T>(tr_operand<STR>(Qs + buf + tr_off, 32 * qb + 16 * t, 32 * db), bds[t], dkacc[db]);
+                }
+        }
+        if (more) {
+            qc.store(Qs + TILE - buf, tid);
+            oc.store(dOs + TILE - buf, tid);
+            store_stats(sb ^ 1);
+        }
+        __syncthreads();
+    }
+
+    stage_transposed<T, D, STR>(Qs, 32 * w + n32, h, dkacc, scale);
+    __syncthreads();
+    store_staged<D, STR>(dK + base, Qs, kK_BK, k0, N, tid);
+    __syncthreads();
+    stage_transposed<T, D, STR>(Qs, 32 * w + n32, h, dvacc, 1.f);
+    __syncthreads();
+    store_staged<D, STR>(dV + base, Qs, kK_BK, k0, N, tid);
+}
+
+template <class T, int D, bool CAUSAL>
+hipError_t launch(const BwdParams& p) {
+    const int ntq = (p.N + kQ_BQ - 1) / kQ_BQ;
+    const int ntk = (p.N + kK_BK - 1) / kK_BK;
+    const int64_t bh = (int64_t)p.B * p.H;
+    if (bh * ntq > 0x7fffffff || bh * ntk > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const float c = p.scale * kLog2e;
+    hipStream_t st = (hipStream_t)p.stream;
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)(bh * ntq)), dim3(kThreads), 0, st,
+                       (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v, (const uint16_t*)p.o,
+                       (const uint16_t*)p.dout, p.lse, p.delta, (uint16_t*)p.dq, p.N, ntq, p.scale, c);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, CAUSAL>), dim3((unsigned)(bh * ntk)), dim3(kThreads), 0, st,
+                       (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v, (const uint16_t*)p.dout,
+                       p.lse, p.delta, (uint16_t*)p.dk, (uint16_t*)p.dv, p.N, ntk, p.scale, c);
+    return hipGetLastError();
+}
+
+template <class T, int D>
+hipError_t launch_c(const BwdParams& p) {
+    return p.causal ? launch<T, D, true>(p) : launch<T, D, false>(p);
+}
+
+template <class T>
+hipError_t launch_d(const BwdParams& p) {
+    return p.d == 64 ? launch_c<T, 64>(p) : launch_c<T, 128>(p);
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdParams& p) {
+    return p.dtype == kDtypeBF16 ? launch_d<BF16>(p) : launch_d<F16>(p);
+}
 
 }  // namespace attn

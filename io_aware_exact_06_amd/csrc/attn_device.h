@@ -99,6 +99,91 @@ __device__ inline float sum_with_other_half(float x) {
     return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
 
+// LDS row stride (in 16-bit elements) of a tile with D columns.  LDS has 64
+// banks of 4 bytes; a 128-bit read is served 16 lanes at a time, and a
+// transpose read serves 16-lane groups that each touch 4 rows x 32 bytes.
+// A stride of 76 dwords (D = 128) or 36 dwords (D = 64) keeps both access
+// kinds free of bank conflicts (measured on gfx950: ~200 B/clk/CU for
+// 128-bit reads, ~100 B/clk/CU for transpose reads).
+template <int D>
+struct LdsStride;
+template <>
+struct LdsStride<128> {
+    static constexpr int value = 152;
+};
+template <>
+struct LdsStride<64> {
+    static constexpr int value = 72;
+};
+
+// Copy a tile of ROWS x D 16-bit values (rows r0 .. r0+ROWS-1 of a row-major
+// [nrows, D] array) from global memory into registers, 16 bytes per chunk;
+// rows at or beyond nrows read as zero.  THREADS threads split the tile.
+template <int ROWS, int D, int THREADS>
+struct TileCopy {
+    static constexpr int CH = D / 8;                      // 16-byte chunks per row
+    static constexpr int CPT = ROWS * CH / THREADS;       // chunks per thread
+    static_assert(ROWS * CH % THREADS == 0, "tile must split evenly over the threads");
+    static constexpr int STR = LdsStride<D>::value;
+
+    u32x4 r[CPT];
+
+    __device__ inline void load(const uint16_t* __restrict__ src, int r0, int nrows, int tid) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + i * THREADS;
+            const int row = c / CH, col = c % CH;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            r[i] = (r0 + row < nrows) ? *(const u32x4*)(src + (int64_t)(r0 + row) * D + 8 * col) : z;
+        }
+    }
+
+    __device__ inline void store(uint16_t* dst, int tid) const {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + i * THREADS;
+            const int row = c / CH, col = c % CH;
+            *(u32x4*)(dst + row * STR + 8 * col) = r[i];
+        }
+    }
+};
+
+// Offset (in elements, relative to the start of a 32-column block of a 16-row
+// step) of this lane's address for the transpose read that yields the A
+// operand A[m][k] = T[row(k)][col0 + m] of a 32x32x16 MFMA from a row-major
+// LDS tile T: 16-lane group g reads columns 16*(g%2) .. +15 and rows
+// 4*(lane/32) .. +3; a second read 8 rows further supplies k = 4..7.  With
+// this, logical k = 8*(l/32) + e maps to row 8*(e/4) + 4*(l/32) + e%4 of the
+// step, which is exactly the row order of a 32x32 accumulator's elements.
+template <int STR>
+__device__ inline int tr_lane_offset(int lane) {
+    const int g16 = lane & 15;
+    return ((g16 >> 2) + 4 * (lane >> 5)) * STR + 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);
+}
+
+// A operand (M = 32 columns starting at col0, K = 16 rows starting at row0)
+// read transposed from a row-major LDS tile, for the lane offset above.
+template <int STR>
+__device__ inline u32x4 tr_operand(const uint16_t* tile_at_lane, int row0, int col0) {
+    const uint16_t* p = tile_at_lane + row0 * STR + col0;
+    const u32x2 lo = lds_read_tr(p);
+    const u32x2 hi = lds_read_tr(p + 8 * STR);
+    const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+    return a;
+}
+
+// Pack the 16 fp32 accumulator values of a 32x32 MFMA result (lane l: column
+// l % 32, rows 8*(e/4) + 4*(l/32) + e%4) into the B operands of two 16-deep
+// k-steps that contract over those rows: k-step t takes elements 8t .. 8t+7.
+template <class T>
+__device__ inline void pack_acc_as_b(const f32x16& v, u32x4& b0, u32x4& b1) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        b0[e >> 1] = pack2<T>(v[e], v[e + 1]);
+        b1[e >> 1] = pack2<T>(v[8 + e], v[8 + e + 1]);
+    }
+}
+
 // Work groups are handed to the 8 XCDs round-robin (block b runs on XCD b % 8).
 // Renumber them so that each XCD receives one contiguous range of work items:
 // consecutive items (the tiles of one head) then share that XCD's L2.

@@ -42,41 +42,14 @@ constexpr int kThreads = kWaves * 64;
 
 template <int D>
 struct FwdShape {
-    static constexpr int KS = D / 16;                       // MFMA k-steps of S^T over d
-    static constexpr int DB = D / 32;                       // 32-row blocks of O^T
-    static constexpr int KB = kBK / 32;                     // 32-key blocks of a tile
-    static constexpr int STR = D + 8;                       // LDS row stride in elements (pad 16 B)
-    static constexpr int CH = D / 8;                        // 16-byte chunks per row
-    static constexpr int CPT = kBK * CH / kThreads;         // chunks per thread per tile
-    static constexpr int TILE = kBK * STR;                  // elements per LDS tile
-    static_assert(kBK * CH % kThreads == 0, "tile must split evenly over the threads");
+    static constexpr int KS = D / 16;                 // MFMA k-steps of S^T over d
+    static constexpr int DB = D / 32;                 // 32-row blocks of O^T
+    static constexpr int KB = kBK / 32;               // 32-key blocks of a tile
+    static constexpr int STR = LdsStride<D>::value;   // LDS row stride in elements
+    static constexpr int CH = D / 8;                  // 16-byte chunks per row
+    static constexpr int TILE = kBK * STR;            // elements per LDS tile
     static_assert(kBQ * STR <= 2 * TILE, "output staging must fit in the K buffers");
 };
-
-template <int D>
-__device__ inline void load_tile(const uint16_t* __restrict__ src, int k0, int N, int tid,
-                                 u32x4 (&r)[FwdShape<D>::CPT]) {
-    using S = FwdShape<D>;
-#pragma unroll
-    for (int i = 0; i < S::CPT; ++i) {
-        const int c = tid + i * kThreads;
-        const int row = c / S::CH, col = c % S::CH;
-        const int key = k0 + row;
-        u32x4 z = {0u, 0u, 0u, 0u};
-        r[i] = key < N ? *(const u32x4*)(src + (int64_t)key * D + 8 * col) : z;
-    }
-}
-
-template <int D>
-__device__ inline void store_tile(uint16_t* dst, int tid, const u32x4 (&r)[FwdShape<D>::CPT]) {
-    using S = FwdShape<D>;
-#pragma unroll
-    for (int i = 0; i < S::CPT; ++i) {
-        const int c = tid + i * kThreads;
-        const int row = c / S::CH, col = c % S::CH;
-        *(u32x4*)(dst + row * S::STR + 8 * col) = r[i];
-    }
-}
 
 template <class T, int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
@@ -114,11 +87,11 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     const int kend = CAUSAL ? min(N, q0 + kBQ) : N;
     const int nkt = (kend + kBK - 1) / kBK;
 
-    u32x4 kr[S::CPT], vr[S::CPT];
-    load_tile<D>(Kh, 0, N, tid, kr);
-    load_tile<D>(Vh, 0, N, tid, vr);
-    store_tile<D>(Ks, tid, kr);
-    store_tile<D>(Vs, tid, vr);
+    TileCopy<kBK, D, kThreads> kc, vc;
+    kc.load(Kh, 0, N, tid);
+    vc.load(Vh, 0, N, tid);
+    kc.store(Ks, tid);
+    vc.store(Vs, tid);
     __syncthreads();
 
     f32x16 oacc[S::DB];
@@ -129,19 +102,15 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     float m = kNegInf;  // running maximum of the raw scores of row qrow
     float l = 0.f;      // this lane's share of the running sum (its 16 keys of every 32)
 
-    // Transpose-read addressing for V^T (see lds_read_tr): 16-lane group g
-    // covers d columns 16*(g%2) .. +15 of a 32-column block and key rows
-    // 4*h .. 4*h + 3 (+8) of a 16-key step.
-    const int g16 = lane & 15;
-    const int tr_off = (g16 >> 2) * S::STR + 16 * ((lane >> 4) & 1) + 4 * (g16 & 3) + 4 * h * S::STR;
+    const int tr_off = tr_lane_offset<S::STR>(lane);  // V^T read transposed from the V tile
 
     for (int jt = 0; jt < nkt; ++jt) {
         const int buf = (jt & 1) * S::TILE;
         const int k0 = jt * kBK;
         const bool more = jt + 1 < nkt;
         if (more) {
-            load_tile<D>(Kh, k0 + kBK, N, tid, kr);
-            load_tile<D>(Vh, k0 + kBK, N, tid, vr);
+            kc.load(Kh, k0 + kBK, N, tid);
+            vc.load(Vh, k0 + kBK, N, tid);
         }
         const bool active = !CAUSAL || k0 <= wq0 + kRowsPerWave - 1;
         if (active) {
@@ -188,20 +157,17 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             // ---- P^T = exp2(c*s - c*m), packed as the B operand of O^T += V^T P^T
             u32x4 pf[S::KB][2];
 #pragma unroll
-            for (int kb = 0; kb < S::KB; ++kb)
+            for (int kb = 0; kb < S::KB; ++kb) {
+                f32x16 p;
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int e = 0; e < 8; e += 2) {
-                        float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * t + e], c, -mc));
-                        float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * t + e + 1], c, -mc));
-                        if (masked) {
-                            p0 = s[kb][8 * t + e] == kNegInf ? 0.f : p0;
-                            p1 = s[kb][8 * t + e + 1] == kNegInf ? 0.f : p1;
-                        }
-                        l += p0 + p1;
-                        pf[kb][t][e >> 1] = pack2<T>(p0, p1);
-                    }
+                for (int e = 0; e < 16; ++e) {
+                    float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e], c, -mc));
+                    if (masked) pe = s[kb][e] == kNegInf ? 0.f : pe;
+                    l += pe;
+                    p[e] = pe;
+                }
+                pack_acc_as_b<T>(p, pf[kb][0], pf[kb][1]);
+            }
             // ---- O^T += V^T P^T
             const uint16_t* vp = Vs + buf + tr_off;
 #pragma unroll
@@ -209,18 +175,12 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #pragma unroll
                 for (int kb = 0; kb < S::KB; ++kb)
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const uint16_t* p = vp + (kb * 32 + 16 * t) * S::STR + 32 * db;
-                        const u32x2 lo = lds_read_tr(p);
-                        const u32x2 hi = lds_read_tr(p + 8 * S::STR);
-                        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-                        oacc[db] = mfma32<T>(a, pf[kb][t], oacc[db]);
-                    }
+                    for (int t = 0; t < 2; ++t)
+                        oacc[db] = mfma32<T>(tr_operand<S::STR>(vp, kb * 32 + 16 * t, 32 * db), pf[kb][t], oacc[db]);
         }
         if (more) {
-            const int nbuf = S::TILE - buf;
-            store_tile<D>(Ks + nbuf, tid, kr);
-            store_tile<D>(Vs + nbuf, tid, vr);
+            kc.store(Ks + S::TILE - buf, tid);
+            vc.store(Vs + S::TILE - buf, tid);
         }
         __syncthreads();
     }

@@ -32,27 +32,15 @@ struct BwdParams {
     void* dq;
     void* dk;
     void* dv;
-    float* dq_acc;  // fp32 [B, H, N, d], part of the caller's workspace
-    float* delta;   // fp32 [B, H, N], part of the caller's workspace
+    float* delta;  // fp32 [B, H, N] row terms D_i = <dO_i, O_i>: the caller's workspace
     int B, H, N, d, causal, dtype;
     float scale;
     void* stream;
 };
 
-// Byte offsets of the backward workspace regions (256-byte aligned).
-struct BwdWorkspaceLayout {
-    size_t dq_acc_offset, delta_offset, total;
-};
-
-inline size_t round_up_256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-inline BwdWorkspaceLayout bwd_workspace_layout(int64_t B, int64_t H, int64_t N, int64_t d) {
-    BwdWorkspaceLayout w;
-    const size_t rows = (size_t)(B * H * N);
-    w.dq_acc_offset = 0;
-    w.delta_offset = round_up_256(rows * (size_t)d * sizeof(float));
-    w.total = w.delta_offset + round_up_256(rows * sizeof(float));
-    return w;
+// Bytes of backward workspace: one fp32 D per query row, rounded up to 256.
+inline size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t N) {
+    return (((size_t)(B * H * N) * sizeof(float)) + 255) & ~(size_t)255;
 }
 
 hipError_t launch_fwd(const FwdParams& p);

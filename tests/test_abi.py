@@ -76,7 +76,7 @@ def test_fwd_empty_problem_is_a_no_op():
 def test_bwd_workspace_bytes():
     B, H, N, d = 2, 3, 100, 128
     n = attn.attn_bwd_workspace_bytes(B, H, N, d)
-    assert n >= B * H * N * (d + 1) * 4
+    assert n >= B * H * N * 4 and n % 256 == 0
     assert attn.attn_bwd_workspace_bytes(0, 3, 100, 128) == 0
     assert attn.attn_bwd_workspace_bytes(-1, 3, 100, 128) == ctypes.c_size_t(-1).value
 

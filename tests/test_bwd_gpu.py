@@ -1,0 +1,121 @@
+"""Backward parity on the GPU: dQ, dK, dV from the HIP kernels (through the C ABI,
+fed with the GPU forward's O and lse) against the fp64 oracle's analytic gradients.
+
+Small shapes compare whole tensors (relative L2 <= 1e-2 per tensor); the two
+backward workloads at full size compare sampled rows of dQ and sampled key
+rows of dK, dV for a few heads, plus invariants that hold at any size.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from io_aware_exact_06_amd import attn
+from io_aware_exact_06_amd.inputs import WORKLOADS, default_scale, make_inputs, workload_inputs
+from tests.tolerance import GRAD_TOL, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_fwd_bwd(inp, causal, scale):
+    q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "dout"))
+    o, lse = attn.fwd(q, k, v, causal, scale)
+    dq, dk, dv = attn.bwd(q, k, v, o, do, lse, causal, scale)
+    torch.cuda.synchronize()
+    return [t.float().cpu().numpy() for t in (dq, dk, dv)]
+
+
+def heads(t):
+    B, H, N, d = t.shape
+    return t.double().numpy().reshape(B * H, N, d)
+
+
+SMALL = [
+    # B, H, N, d, dtype, causal
+    (1, 2, 64, 128, "bf16", False),
+    (1, 2, 300, 128, "bf16", True),
+    (2, 2, 1, 64, "f16", True),
+    (1, 1, 33, 128, "f16", False),
+    (1, 2, 129, 64, "bf16", True),
+    (2, 1, 191, 64, "f16", True),
+    (1, 2, 700, 128, "f16", True),
+    (1, 2, 517, 64, "bf16", False),
+    (1, 1, 256, 64, "f16", False),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype,causal", SMALL)
+def test_bwd_small_full(B, H, N, d, dtype, causal):
+    label = "bwd small B%d H%d N%d d%d %s causal=%d" % (B, H, N, d, dtype, causal)
+    say(label)
+    inp = make_inputs(B, H, N, d, dtype, seed=N * 11 + d + causal, with_dout=True)
+    scale = default_scale(d)
+    g = gpu_fwd_bwd(inp, causal, scale)
+    ref = oracle.bwd(heads(inp["q"]), heads(inp["k"]), heads(inp["v"]), heads(inp["dout"]), causal, scale)
+    errs = [rel_l2(a.reshape(B * H, N, d), r) for a, r in zip(g, ref)]
+    say("  rel-L2 dq %.3g dk %.3g dv %.3g" % tuple(errs))
+    assert max(errs) <= GRAD_TOL, errs
+
+
+def sample(n, rng, extra=40):
+    fixed = [0, 1, 63, 64, 127, 128, n // 2, n - 2, n - 1]
+    s = set(r for r in fixed if 0 <= r < n)
+    s.update(int(x) for x in rng.choice(n, size=min(extra, n), replace=False))
+    return np.array(sorted(s))
+
+
+@pytest.mark.parametrize("idx", [3, 4])
+def test_bwd_workload_sampled(idx):
+    w = WORKLOADS[idx]
+    say("bwd workload %s (sampled rows and keys)" % w.name)
+    inp = workload_inputs(idx)
+    scale = default_scale(w.d)
+    dq, dk, dv = (a.reshape(-1, w.N, w.d) for a in gpu_fwd_bwd(inp, w.causal, scale))
+    rng = np.random.default_rng(100 + idx)
+    BH = w.B * w.H
+    hsel = sorted(set([0, BH - 1, int(rng.integers(BH))]))
+    rows, keys = sample(w.N, rng), sample(w.N, rng)
+    q, k, v, do = (heads(inp[n])[hsel] for n in ("q", "k", "v", "dout"))
+    rq, rk, rv = oracle.bwd(q, k, v, do, w.causal, scale, rows=rows, keys=keys)
+    errs = [rel_l2(dq[hsel][:, rows], rq), rel_l2(dk[hsel][:, keys], rk), rel_l2(dv[hsel][:, keys], rv)]
+    say("  rel-L2 dq %.3g dk %.3g dv %.3g" % tuple(errs))
+    assert max(errs) <= GRAD_TOL, errs
+
+
+@pytest.mark.parametrize("idx", [3, 4])
+def test_bwd_invariants_full_size(idx):
+    """sum_j dV_j = sum_i dO_i and sum_j dK_j = 0 (rows of P sum to one, rows of dS to zero);
+    V = 1 gives dQ = dK = 0; dO = 0 gives all-zero gradients."""
+    w = WORKLOADS[idx]
+    say("bwd invariants at full size: %s" % w.name)
+    inp = workload_inputs(idx)
+    scale = default_scale(w.d)
+    dq, dk, dv = (torch.from_numpy(a).double() for a in gpu_fwd_bwd(inp, w.causal, scale))
+    do = inp["dout"].double()
+    e_v = rel_l2(dv.sum(2).numpy(), do.sum(2).numpy())
+    e_k = float(dk.sum(2).norm() / dk.abs().sum(2).norm())
+    say("  sum dV vs sum dO rel %.3g; |sum dK| / |sum |dK|| %.3g" % (e_v, e_k))
+    assert e_v <= GRAD_TOL and e_k <= GRAD_TOL
+    ones = dict(inp, v=torch.ones_like(inp["v"]))
+    dq1, dk1, dv1 = gpu_fwd_bwd(ones, w.causal, scale)
+    ratio = max(np.abs(dq1).max(), np.abs(dk1).max()) / np.abs(dv1).max()
+    say("  V=1: max|dQ|,|dK| / max|dV| = %.3g" % ratio)
+    assert ratio <= 1e-3
+    zero = dict(inp, dout=torch.zeros_like(inp["dout"]))
+    z = gpu_fwd_bwd(zero, w.causal, scale)
+    assert all(np.all(a == 0.0) for a in z)
+
+
+def test_bwd_deterministic():
+    say("bwd determinism")
+    inp = make_inputs(1, 3, 555, 128, "bf16", seed=77, with_dout=True)
+    a = gpu_fwd_bwd(inp, True, 0.09)
+    b = gpu_fwd_bwd(inp, True, 0.09)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
