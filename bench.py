@@ -38,28 +38,33 @@ def flops(w, passes):
     return f, (b if "bwd" in passes else 0.0)
 
 
-def cpu_baseline(w, inp, scale, passes):
-    """The fp64 oracle on the host's cores, on one head of the workload."""
-    import numpy as np
+def cpu_baseline(w, inp, scale, passes, budget_s=10.0):
+    """The fp64 oracle on the host's cores, on whole heads of the workload.
 
+    Heads (b=0, h=0), (b=0, h=1), ... are run one after another (forward, then
+    backward when timed) until about `budget_s` seconds of oracle work have
+    been spent; the rate uses the same FLOP count as the GPU.
+    """
     import oracle
-    q, k, v = (inp[n][0, 0].double().numpy()[None] for n in ("q", "k", "v"))
     pairs = w.pairs_per_head()
-    t0 = time.perf_counter()
-    oracle.fwd(q, k, v, w.causal, scale)
-    t_f = time.perf_counter() - t0
-    fl = 4.0 * w.d * pairs
-    t = t_f
-    sample = "head (b=0,h=0) of the workload, forward"
-    if "bwd" in passes and t_f < 15.0:
-        do = inp["dout"][0, 0].double().numpy()[None]
+    per_head = 4.0 * w.d * pairs + (10.0 * w.d * pairs if "bwd" in passes else 0.0)
+    total_t, heads = 0.0, 0
+    for h in range(w.B * w.H):
+        b, hh = divmod(h, w.H)
+        q, k, v = (inp[n][b, hh].double().numpy()[None] for n in ("q", "k", "v"))
         t0 = time.perf_counter()
-        oracle.bwd(q, k, v, do, w.causal, scale)
-        t += time.perf_counter() - t0
-        fl += 10.0 * w.d * pairs
-        sample = "head (b=0,h=0) of the workload, forward + backward"
-    return {"value": fl / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "sample": sample + " (N=%d, d=%d, causal), %.1f s" % (w.N, w.d, t),
+        oracle.fwd(q, k, v, w.causal, scale)
+        if "bwd" in passes:
+            oracle.bwd(q, k, v, inp["dout"][b, hh].double().numpy()[None], w.causal, scale)
+        total_t += time.perf_counter() - t0
+        heads += 1
+        if total_t >= budget_s:
+            break
+    what = "forward + backward" if "bwd" in passes else "forward"
+    return {"value": per_head * heads / total_t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "%d of %d heads of the workload (N=%d, d=%d, causal=%s), %s, %.1f s"
+                      % (heads, w.B * w.H, w.N, w.d, w.causal, what, total_t),
             "cpu": platform.processor() or platform.machine()}
 
 
@@ -129,9 +134,13 @@ def main():
     f_tf = ff / (sum(fwd_ms) / len(fwd_ms) * 1e-3) / 1e12
     b_tf = fb / (sum(bwd_ms) / len(bwd_ms) * 1e-3) / 1e12 if bwd else None
     value = (ff + fb) / (ms_step * 1e-3) / 1e12
-    # Dominant kernel: the backward pass when it runs, else the forward.
+    # Dominant work: the backward pass (attn_bwd_dq_kernel then attn_bwd_dkdv_kernel,
+    # timed together by the events around one attn_bwd call) when it runs, else the forward.
+    fwd_roof = {"bound": "mfma", "achieved": round(f_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(f_tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": "attn_fwd_kernel",
+                "avg_ms": round(sum(fwd_ms) / len(fwd_ms), 4)}
     if bwd:
-        dom = {"kernel": "attn_bwd (dK/dV/dQ main kernel + D and dQ-convert passes)",
+        dom = {"kernel": "attn_bwd pass: attn_bwd_dq_kernel + attn_bwd_dkdv_kernel",
                "achieved": b_tf, "avg_ms": sum(bwd_ms) / len(bwd_ms)}
     else:
         dom = {"kernel": "attn_fwd_kernel", "achieved": f_tf, "avg_ms": sum(fwd_ms) / len(fwd_ms)}
@@ -155,6 +164,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(dom["achieved"], 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(dom["achieved"] / PEAK_BF16_TFLOPS, 4),
                      "traffic": None, "kernel": dom["kernel"], "avg_ms": round(dom["avg_ms"], 4)},
+        "roofline_fwd": fwd_roof,
         "outputs_finite": finite,
     }
     if bwd:
