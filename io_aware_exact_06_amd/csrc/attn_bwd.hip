@@ -96,7 +96,7 @@ constexpr int kQ_BQ = 128;
 constexpr int kQ_BK = 64;
 
 template <class T, int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                         const uint16_t* __restrict__ V, const uint16_t* __restrict__ O,
                         const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
@@ -122,29 +122,33 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     const int qrow = wq0 + n32;
     const bool valid = qrow < N;
 
-    // Resident Q^T and dO^T fragments; D = <dO, O> for this row.
+    // Resident Q^T and dO^T fragments; D = <dO, O> for this row.  Rows past
+    // the end read row N-1: their D is not stored, their lse is +inf (P = 0),
+    // and their dQ is not written.
     u32x4 qf[KS], dof[KS];
     float dpart = 0.f;
+    const int qrd = min(qrow, N - 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        const int64_t off = (int64_t)qrow * D + 16 * ks + 8 * h;
-        qf[ks] = valid ? *(const u32x4*)(Qh + off) : z;
-        dof[ks] = valid ? *(const u32x4*)(dOh + off) : z;
-        const u32x4 of = valid ? *(const u32x4*)(Oh + off) : z;
+        const int64_t off = (int64_t)qrd * D + 16 * ks + 8 * h;
+        qf[ks] = *(const u32x4*)(Qh + off);
+        dof[ks] = *(const u32x4*)(dOh + off);
+        const u32x4 of = *(const u32x4*)(Oh + off);
         dpart += dot8<T>(dof[ks], of);
     }
     const float Dq = sum_with_other_half(dpart);
     if (h == 0 && valid) Delta[(int64_t)bh * N + qrow] = Dq;
-    const float lse2 = valid ? LSE[(int64_t)bh * N + qrow] * kLog2e : kPosInf;
+    const float lse2 = valid ? LSE[(int64_t)bh * N + qrd] * kLog2e : kPosInf;
 
     const int kend = CAUSAL ? min(N, q0 + kQ_BQ) : N;
     const int nkt = (kend + kQ_BK - 1) / kQ_BK;
-    Copy kc, vc;
+    // Leading key tiles visible in full to every row of the group.
+    const int nfull = min(N / kQ_BK, CAUSAL ? (q0 + 1) / kQ_BK : N / kQ_BK);
+    Copy kc(tid), vc(tid);
     kc.load(Kh, 0, N, tid);
     vc.load(Vh, 0, N, tid);
-    kc.store(Ks, tid);
-    vc.store(Vs, tid);
+    kc.store(Ks);
+    vc.store(Vs);
     __syncthreads();
 
     f32x16 dqacc[DB];
@@ -154,7 +158,8 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
         for (int e = 0; e < 16; ++e) dqacc[db][e] = 0.f;
     const int tr_off = tr_lane_offset<STR>(lane);
 
-    for (int jt = 0; jt < nkt; ++jt) {
+    auto step = [&](int jt, auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
         const int buf = (jt & 1) * TILE;
         const int k0 = jt * kQ_BK;
         const bool more = jt + 1 < nkt;
@@ -162,8 +167,10 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
             kc.load(Kh, k0 + kQ_BK, N, tid);
             vc.load(Vh, k0 + kQ_BK, N, tid);
         }
-        if (!CAUSAL || k0 <= wq0 + 31) {
+        if (!(MASKED && CAUSAL) || k0 <= wq0 + 31) {
+            // ---- S^T = K Q^T and dP^T = V dO^T
             f32x16 s[KB], dp[KB];
+            prio_mfma();
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -178,7 +185,9 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                     dp[kb] = mfma32<T>(*(const u32x4*)(Vs + roff + 16 * ks), dof[ks], dp[kb]);
                 }
             }
-            const bool masked = (k0 + kQ_BK > N) || (CAUSAL && k0 + kQ_BK - 1 > wq0);
+            sched_reads_ahead<4, 2 * KB * KS, 1>();
+            prio_normal();
+            // ---- P^T = exp(scale s - lse), dS^T = P^T o (dP^T - D)
             u32x4 b[KB][2];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
@@ -186,7 +195,7 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e], c, -lse2));
-                    if (masked) {
+                    if constexpr (MASKED) {
                         const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
                         if (key >= N || (CAUSAL && key > qrow)) p = 0.f;
                     }
@@ -194,7 +203,9 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                 }
                 pack_acc_as_b<T>(ds, b[kb][0], b[kb][1]);
             }
+            // ---- dQ^T += K^T dS^T
             const uint16_t* kt = Ks + buf + tr_off;
+            prio_mfma();
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -202,13 +213,17 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 #pragma unroll
                     for (int t = 0; t < 2; ++t)
                         dqacc[db] = mfma32<T>(tr_operand<STR>(kt, kb * 32 + 16 * t, 32 * db), b[kb][t], dqacc[db]);
+            sched_reads_ahead<8, DB * KB * 2, 2>();
+            prio_normal();
         }
         if (more) {
-            kc.store(Ks + TILE - buf, tid);
-            vc.store(Vs + TILE - buf, tid);
+            kc.store(Ks + TILE - buf);
+            vc.store(Vs + TILE - buf);
         }
         __syncthreads();
-    }
+    };
+    for (int jt = 0; jt < nfull; ++jt) step(jt, Flag<false>{});
+    for (int jt = nfull; jt < nkt; ++jt) step(jt, Flag<true>{});
 
     stage_transposed<T, D, STR>(Ks, 32 * w + n32, h, dqacc, scale);
     __syncthreads();
@@ -217,12 +232,15 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 
 // ============================================================================
 // dK and dV: one work group per (batch*head, 128 key rows), 4 waves x 32 keys.
+// At d = 128 the resident K, V fragments and both accumulators need more than
+// the 256 registers of a two-waves-per-SIMD budget, so this kernel runs one
+// wave per SIMD there (forcing two spills heavily); at d = 64 it runs two.
 // ============================================================================
 constexpr int kK_BK = 128;
 constexpr int kK_BQ = 64;
 
 template <class T, int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(D == 64 ? 2 : 1, 2)))
 void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                           const float* __restrict__ LSE, const float* __restrict__ Delta,
@@ -251,18 +269,22 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     const int krow = wk0 + n32;
 
     // Resident K and V fragments (B operands of S = Q K^T and dP = dO V^T).
+    // Keys past the end read row N-1; their dK and dV are never written.
     u32x4 kf[KS], vf[KS];
+    const int krd = min(krow, N - 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        const int64_t off = (int64_t)krow * D + 16 * ks + 8 * h;
-        kf[ks] = krow < N ? *(const u32x4*)(Kh + off) : z;
-        vf[ks] = krow < N ? *(const u32x4*)(Vh + off) : z;
+        const int64_t off = (int64_t)krd * D + 16 * ks + 8 * h;
+        kf[ks] = *(const u32x4*)(Kh + off);
+        vf[ks] = *(const u32x4*)(Vh + off);
     }
 
     const int q_start = CAUSAL ? (k0 / kK_BQ) * kK_BQ : 0;
     const int nqt = (N - q_start + kK_BQ - 1) / kK_BQ;
-    Copy qc, oc;
+    // Query tiles that straddle the keys of the group need the causal mask;
+    // rows past the end need none (their lse is +inf, so P = 0).
+    const int nmask = CAUSAL ? min(nqt, (k0 + kK_BK - q_start + kK_BQ - 1) / kK_BQ) : 0;
+    Copy qc(tid), oc(tid);
     float st_l = kPosInf, st_d = 0.f;
     auto load_stats = [&](int r0) {
         if (tid < kK_BQ) {
@@ -271,17 +293,17 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
             st_d = r < N ? Dh[r] : 0.f;
         }
     };
-    auto store_stats = [&](int b) {
+    auto store_stats = [&](int sb) {
         if (tid < kK_BQ) {
-            stats[b][0][tid] = st_l;
-            stats[b][1][tid] = st_d;
+            stats[sb][0][tid] = st_l;
+            stats[sb][1][tid] = st_d;
         }
     };
     qc.load(Qh, q_start, N, tid);
     oc.load(dOh, q_start, N, tid);
     load_stats(q_start);
-    qc.store(Qs, tid);
-    oc.store(dOs, tid);
+    qc.store(Qs);
+    oc.store(dOs);
     store_stats(0);
     __syncthreads();
 
@@ -295,7 +317,8 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         }
     const int tr_off = tr_lane_offset<STR>(lane);
 
-    for (int it = 0; it < nqt; ++it) {
+    auto step = [&](int it, auto masked_tag) {
+        constexpr bool MASKED = decltype(masked_tag)::value;
         const int sb = it & 1;
         const int buf = sb * TILE;
         const int qq0 = q_start + it * kK_BQ;
@@ -308,7 +331,8 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const int qb0 = qq0 + 32 * qb;  // first query row of this 32-row block
-            if (CAUSAL && qb0 + 31 < wk0) continue;  // every query precedes every key of this wave
+            if (MASKED && qb0 + 31 < wk0) continue;  // every query precedes every key of this wave
+            // ---- S = Q K^T and dP = dO V^T
             f32x16 s, dp;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
@@ -316,11 +340,14 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
                 dp[e] = 0.f;
             }
             const int roff = buf + (32 * qb + n32) * STR + 8 * h;
+            prio_mfma();
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 s = mfma32<T>(*(const u32x4*)(Qs + roff + 16 * ks), kf[ks], s);
                 dp = mfma32<T>(*(const u32x4*)(dOs + roff + 16 * ks), vf[ks], dp);
             }
+            sched_reads_ahead<4, 2 * KS, 1>();
+            prio_normal();
             // Row statistics of the 16 query rows this lane holds: rows 8g + 4h + (0..3).
             f32x16 ls, dd;
 #pragma unroll
@@ -333,18 +360,22 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
                     dd[4 * g + i] = d4[i];
                 }
             }
-            const bool masked = CAUSAL && qb0 < wk0 + 31;
+            // ---- P = exp(scale s - lse), dS = P o (dP - D)
             f32x16 p, ds;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -ls[e]));
-                if (masked && qb0 + 8 * (e >> 2) + 4 * h + (e & 3) < krow) pe = 0.f;
+                if constexpr (MASKED) {
+                    if (qb0 + 8 * (e >> 2) + 4 * h + (e & 3) < krow) pe = 0.f;
+                }
                 p[e] = pe;
                 ds[e] = pe * (dp[e] - dd[e]);
             }
             u32x4 bp[2], bds[2];
             pack_acc_as_b<T>(p, bp[0], bp[1]);
             pack_acc_as_b<T>(ds, bds[0], bds[1]);
+            // ---- dV^T += dO^T P and dK^T += Q^T dS
+            prio_mfma();
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -352,14 +383,18 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
                     dvacc[db] = mfma32<T>(tr_operand<STR>(dOs + buf + tr_off, 32 * qb + 16 * t, 32 * db), bp[t], dvacc[db]);
                     dkacc[db] = mfma32<T>(tr_operand<STR>(Qs + buf + tr_off, 32 * qb + 16 * t, 32 * db), bds[t], dkacc[db]);
                 }
+            sched_reads_ahead<8, DB * 4, 2>();
+            prio_normal();
         }
         if (more) {
-            qc.store(Qs + TILE - buf, tid);
-            oc.store(dOs + TILE - buf, tid);
+            qc.store(Qs + TILE - buf);
+            oc.store(dOs + TILE - buf);
             store_stats(sb ^ 1);
         }
         __syncthreads();
-    }
+    };
+    for (int it = 0; it < nmask; ++it) step(it, Flag<true>{});
+    for (int it = nmask; it < nqt; ++it) step(it, Flag<false>{});
 
     stage_transposed<T, D, STR>(Qs, 32 * w + n32, h, dkacc, scale);
     __syncthreads();

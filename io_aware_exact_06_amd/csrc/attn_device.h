@@ -27,6 +27,12 @@ struct BF16 {};
 struct F16 {};
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Compile-time flag passed to generic lambdas (e.g. masked / unmasked tiles).
+template <bool B>
+struct Flag {
+    static constexpr bool value = B;
+};
 constexpr float kNegInf = -__builtin_inff();
 
 // D(32x32, fp32) += A(32x16) * B(16x32), 16-bit inputs.
@@ -107,9 +113,12 @@ __device__ inline float sum_with_other_half(float x) {
 // 128-bit reads, ~100 B/clk/CU for transpose reads).
 template <int D>
 struct LdsStride;
+#ifndef ATTN_LDS_STRIDE_128
+#define ATTN_LDS_STRIDE_128 152
+#endif
 template <>
 struct LdsStride<128> {
-    static constexpr int value = 152;
+    static constexpr int value = ATTN_LDS_STRIDE_128;
 };
 template <>
 struct LdsStride<64> {
@@ -117,8 +126,17 @@ struct LdsStride<64> {
 };
 
 // Copy a tile of ROWS x D 16-bit values (rows r0 .. r0+ROWS-1 of a row-major
-// [nrows, D] array) from global memory into registers, 16 bytes per chunk;
-// rows at or beyond nrows read as zero.  THREADS threads split the tile.
+// [nrows, D] array, nrows >= 1) from global memory into registers, 16 bytes
+// per chunk, then into an LDS tile of row stride LdsStride<D>.
+//
+// Each thread's chunk offsets inside a tile are computed once and stay in
+// registers for the whole loop; the tile's base address is wave-uniform.  A
+// load is then one instruction on an SGPR base plus a fixed VGPR offset, and
+// no address register is ever recycled while a prefetch is still in flight
+// (recycling one makes the compiler wait for that prefetch before the next
+// use of the register).  Rows at or beyond nrows read row nrows-1 instead, so
+// every load stays in bounds without exec-mask branches; callers mask or
+// discard the duplicated rows.  THREADS threads split the tile.
 template <int ROWS, int D, int THREADS>
 struct TileCopy {
     static constexpr int CH = D / 8;                      // 16-byte chunks per row
@@ -127,24 +145,36 @@ struct TileCopy {
     static constexpr int STR = LdsStride<D>::value;
 
     u32x4 r[CPT];
+    uint32_t goff[CPT];  // byte offset of chunk i inside a global tile
+    uint32_t loff[CPT];  // element offset of chunk i inside an LDS tile
 
-    __device__ inline void load(const uint16_t* __restrict__ src, int r0, int nrows, int tid) {
+    __device__ inline explicit TileCopy(int tid) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = tid + i * THREADS;
-            const int row = c / CH, col = c % CH;
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            r[i] = (r0 + row < nrows) ? *(const u32x4*)(src + (int64_t)(r0 + row) * D + 8 * col) : z;
+            goff[i] = (uint32_t)((c / CH) * D + 8 * (c % CH)) * 2u;
+            loff[i] = (uint32_t)((c / CH) * STR + 8 * (c % CH));
         }
     }
 
-    __device__ inline void store(uint16_t* dst, int tid) const {
+    __device__ inline void load(const uint16_t* __restrict__ src, int r0, int nrows, int tid) {
+        const char* base = (const char*)(src + (int64_t)r0 * D);
+        if (r0 + ROWS <= nrows) {
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int c = tid + i * THREADS;
-            const int row = c / CH, col = c % CH;
-            *(u32x4*)(dst + row * STR + 8 * col) = r[i];
+            for (int i = 0; i < CPT; ++i) r[i] = *(const u32x4*)(base + goff[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const int c = tid + i * THREADS;
+                const int row = min(c / CH, nrows - 1 - r0);
+                r[i] = *(const u32x4*)(base + (uint32_t)(row * D + 8 * (c % CH)) * 2u);
+            }
         }
+    }
+
+    __device__ inline void store(uint16_t* dst) const {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) *(u32x4*)(dst + loff[i]) = r[i];
     }
 };
 
@@ -183,6 +213,25 @@ __device__ inline void pack_acc_as_b(const f32x16& v, u32x4& b0, u32x4& b1) {
         b1[e >> 1] = pack2<T>(v[8 + e], v[8 + e + 1]);
     }
 }
+
+// Scheduling groups for a run of NMFMA MFMAs fed by LDS reads: the first
+// AHEAD reads are issued up front, then each MFMA is followed by the next
+// PER reads, so every MFMA finds its operands loaded AHEAD/PER MFMAs earlier.
+template <int AHEAD, int NMFMA, int PER>
+__device__ inline void sched_reads_ahead() {
+    constexpr int later = NMFMA * PER - AHEAD;  // reads issued between MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+    for (int i = 0; i < NMFMA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < later / PER) __builtin_amdgcn_sched_group_barrier(0x100, PER, 0);
+    }
+}
+
+// Issue priority around MFMA runs: the wave issuing MFMAs is preferred, so
+// the other wave on the SIMD fills the gaps with VALU work.
+__device__ inline void prio_mfma() { __builtin_amdgcn_s_setprio(1); }
+__device__ inline void prio_normal() { __builtin_amdgcn_s_setprio(0); }
 
 // Work groups are handed to the 8 XCDs round-robin (block b runs on XCD b % 8).
 // Renumber them so that each XCD receives one contiguous range of work items:
