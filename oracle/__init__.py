@@ -50,14 +50,14 @@ class OracleLib:
 
     def __init__(self, path: str):
         lib = ctypes.CDLL(path)
-        lib.oracle_attn_fwd.argtypes = [_I, _I, _I, _I, _P, _P, _P, _PI, ctypes.c_int,
+        lib.oracle_attn_fwd.argtypes = [_I, _I, _I, _I, _P, _P, _P, _PI, ctypes.c_int, _I, _I,
                                         ctypes.c_double, _P, _P]
         lib.oracle_attn_fwd.restype = ctypes.c_int
-        lib.oracle_attn_fwd_online.argtypes = [_I, _I, _I, _I, _P, _P, _P, _PI, ctypes.c_int,
+        lib.oracle_attn_fwd_online.argtypes = [_I, _I, _I, _I, _P, _P, _P, _PI, ctypes.c_int, _I, _I,
                                                ctypes.c_double, _I, _P, _P]
         lib.oracle_attn_fwd_online.restype = ctypes.c_int
-        lib.oracle_attn_bwd.argtypes = [_I, _I, _I, _P, _P, _P, _P, ctypes.c_int, ctypes.c_double,
-                                        _PI, _I, _P, _PI, _I, _P, _P]
+        lib.oracle_attn_bwd.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _PI, ctypes.c_int, _I, _I,
+                                        ctypes.c_double, _PI, _I, _P, _PI, _I, _P, _P]
         lib.oracle_attn_bwd.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
@@ -67,60 +67,64 @@ class OracleLib:
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())
 
-    def fwd(self, q, k, v, causal: bool, scale: float, qpos=None):
+    def fwd(self, q, k, v, causal: bool, scale: float, qpos=None, window=(-1, -1)):
         """Three-pass forward.  Returns (o [G,nq,d], lse [G,nq]).
 
-        qpos gives the sequence position of each query row (default 0..nq-1);
-        with causal=True key j is visible to row i iff j <= qpos[i].
+        qpos gives the key position of each query row (default i + nk - nq:
+        rows aligned to the end of the keys, the identity when nq == nk).  Key
+        j is visible to row i iff (not causal or j <= qpos[i]) and, for a
+        window (wl, wr) with -1 meaning unbounded, qpos[i] - wl <= j <= qpos[i] + wr.
         """
         q, k, v = _f64(q), _f64(k), _f64(v)
         G, nq, d = q.shape
         nk = k.shape[1]
         if k.shape != (G, nk, d) or v.shape != (G, nk, d):
             raise ValueError("shape mismatch")
-        qpos = np.ascontiguousarray(np.arange(nq) if qpos is None else qpos, dtype=np.int64)
-        if qpos.shape != (nq,):
-            raise ValueError("qpos must have one entry per query row")
+        qpos = _qpos(qpos, nq, nk)
         o = np.empty((G, nq, d), np.float64)
         lse = np.empty((G, nq), np.float64)
         rc = self.lib.oracle_attn_fwd(G, nq, nk, d, _ptr(q), _ptr(k), _ptr(v), _iptr(qpos),
-                                      int(bool(causal)), float(scale), _ptr(o), _ptr(lse))
+                                      int(bool(causal)), int(window[0]), int(window[1]), float(scale),
+                                      _ptr(o), _ptr(lse))
         if rc != 0:
             raise MemoryError("oracle_attn_fwd failed (%d)" % rc)
         return o, lse
 
-    def fwd_online(self, q, k, v, causal: bool, scale: float, block: int, qpos=None):
+    def fwd_online(self, q, k, v, causal: bool, scale: float, block: int, qpos=None, window=(-1, -1)):
         """Block-wise running-max forward (the validator).  Returns (o, lse)."""
         q, k, v = _f64(q), _f64(k), _f64(v)
         G, nq, d = q.shape
         nk = k.shape[1]
-        qpos = np.ascontiguousarray(np.arange(nq) if qpos is None else qpos, dtype=np.int64)
+        qpos = _qpos(qpos, nq, nk)
         o = np.empty((G, nq, d), np.float64)
         lse = np.empty((G, nq), np.float64)
         rc = self.lib.oracle_attn_fwd_online(G, nq, nk, d, _ptr(q), _ptr(k), _ptr(v), _iptr(qpos),
-                                             int(bool(causal)), float(scale), int(block),
-                                             _ptr(o), _ptr(lse))
+                                             int(bool(causal)), int(window[0]), int(window[1]),
+                                             float(scale), int(block), _ptr(o), _ptr(lse))
         if rc != 0:
             raise RuntimeError("oracle_attn_fwd_online failed (%d)" % rc)
         return o, lse
 
-    def bwd(self, q, k, v, dout, causal: bool, scale: float, rows=None, keys=None):
+    def bwd(self, q, k, v, dout, causal: bool, scale: float, rows=None, keys=None, qpos=None,
+            window=(-1, -1)):
         """Analytic backward.  Returns (dq, dk, dv).
 
+        q, dout: [G, nq, d]; k, v: [G, nk, d]; qpos and window as in fwd.
         rows / keys select which query rows of dq and which key rows of dk, dv
         are computed (default: all).  dq has shape [G, len(rows), d]; dk, dv
         [G, len(keys), d].  An empty selection computes nothing for that output.
         """
         q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
-        G, n, d = q.shape
-        for a in (k, v, dout):
-            if a.shape != (G, n, d):
-                raise ValueError("shape mismatch")
+        G, nq, d = q.shape
+        nk = k.shape[1]
+        if k.shape != (G, nk, d) or v.shape != (G, nk, d) or dout.shape != (G, nq, d):
+            raise ValueError("shape mismatch")
+        qpos = _qpos(qpos, nq, nk)
         rows_a = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
         keys_a = None if keys is None else np.ascontiguousarray(keys, dtype=np.int64).reshape(-1)
-        nrows = n if rows_a is None else len(rows_a)
-        nkeys = n if keys_a is None else len(keys_a)
-        for sel in (rows_a, keys_a):
+        nrows = nq if rows_a is None else len(rows_a)
+        nkeys = nk if keys_a is None else len(keys_a)
+        for sel, n in ((rows_a, nq), (keys_a, nk)):
             if sel is not None and len(sel) and (sel.min() < 0 or sel.max() >= n):
                 raise IndexError("row/key index out of range")
         dq = np.empty((G, nrows, d), np.float64)
@@ -129,13 +133,22 @@ class OracleLib:
         pad = np.zeros(1, np.int64)  # a valid pointer for an empty selection
         rp = None if rows_a is None else (rows_a if nrows else pad)
         kp = None if keys_a is None else (keys_a if nkeys else pad)
-        rc = self.lib.oracle_attn_bwd(G, n, d, _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
-                                      int(bool(causal)), float(scale),
-                                      _iptr(rp), nrows, _ptr(dq), _iptr(kp), nkeys,
-                                      _ptr(dk), _ptr(dv))
+        rc = self.lib.oracle_attn_bwd(G, nq, nk, d, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _iptr(qpos),
+                                      int(bool(causal)), int(window[0]), int(window[1]), float(scale),
+                                      _iptr(rp), nrows, _ptr(dq), _iptr(kp), nkeys, _ptr(dk), _ptr(dv))
         if rc != 0:
             raise MemoryError("oracle_attn_bwd failed (%d)" % rc)
         return dq, dk, dv
+
+
+def _qpos(qpos, nq, nk):
+    """Key positions of the query rows: rows aligned to the end of the keys by default."""
+    if qpos is None:
+        qpos = np.arange(nq) + (nk - nq)
+    qpos = np.ascontiguousarray(qpos, dtype=np.int64)
+    if qpos.shape != (nq,):
+        raise ValueError("qpos must have one entry per query row")
+    return qpos
 
 
 def _load() -> OracleLib:
@@ -171,18 +184,62 @@ def num_threads() -> int:
     return _load().num_threads()
 
 
-def fwd(q, k, v, causal: bool, scale: float, qpos=None):
-    return _load().fwd(q, k, v, causal, scale, qpos)
+def fwd(q, k, v, causal: bool, scale: float, qpos=None, window=(-1, -1)):
+    return _load().fwd(q, k, v, causal, scale, qpos, window)
 
 
-def fwd_online(q, k, v, causal: bool, scale: float, block: int, qpos=None):
-    return _load().fwd_online(q, k, v, causal, scale, block, qpos)
+def fwd_online(q, k, v, causal: bool, scale: float, block: int, qpos=None, window=(-1, -1)):
+    return _load().fwd_online(q, k, v, causal, scale, block, qpos, window)
 
 
-def bwd(q, k, v, dout, causal: bool, scale: float, rows=None, keys=None):
-    return _load().bwd(q, k, v, dout, causal, scale, rows, keys)
+def bwd(q, k, v, dout, causal: bool, scale: float, rows=None, keys=None, qpos=None, window=(-1, -1)):
+    return _load().bwd(q, k, v, dout, causal, scale, rows, keys, qpos, window)
 
 
 fwd.__doc__ = OracleLib.fwd.__doc__
 fwd_online.__doc__ = OracleLib.fwd_online.__doc__
 bwd.__doc__ = OracleLib.bwd.__doc__
+
+
+def _segments(cu, total):
+    cu = np.asarray(cu, dtype=np.int64).reshape(-1)
+    if len(cu) < 1 or cu[0] != 0 or cu[-1] != total or np.any(np.diff(cu) < 0):
+        raise ValueError("cumulative lengths must start at 0, not decrease and end at the total")
+    return [(int(cu[b]), int(cu[b + 1])) for b in range(len(cu) - 1)]
+
+
+def fwd_varlen(q, k, v, cu_q, cu_k, causal: bool, scale: float, window=(-1, -1)):
+    """Packed variable-length forward: q [H, total_q, d], k, v [H, total_k, d].
+
+    Sequence b owns query rows cu_q[b]..cu_q[b+1]-1 and keys cu_k[b]..cu_k[b+1]-1
+    of every head; each is attended on its own, rows aligned to the end of its
+    keys.  Returns (o [H, total_q, d], lse [H, total_q]).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    H, tq, d = q.shape
+    sq, sk = _segments(cu_q, tq), _segments(cu_k, k.shape[1])
+    if len(sq) != len(sk):
+        raise ValueError("cu_q and cu_k describe different batch sizes")
+    o = np.zeros((H, tq, d))
+    lse = np.full((H, tq), -np.inf)
+    for (q0, q1), (k0, k1) in zip(sq, sk):
+        if q1 == q0:
+            continue
+        if k1 == k0:  # no keys at all: every row sees nothing
+            continue
+        o[:, q0:q1], lse[:, q0:q1] = fwd(q[:, q0:q1], k[:, k0:k1], v[:, k0:k1], causal, scale, window=window)
+    return o, lse
+
+
+def bwd_varlen(q, k, v, dout, cu_q, cu_k, causal: bool, scale: float, window=(-1, -1)):
+    """Packed variable-length backward (layout as fwd_varlen).  Returns (dq, dk, dv)."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    H, tq, d = q.shape
+    sq, sk = _segments(cu_q, tq), _segments(cu_k, k.shape[1])
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for (q0, q1), (k0, k1) in zip(sq, sk):
+        if q1 == q0 or k1 == k0:
+            continue
+        dq[:, q0:q1], dk[:, k0:k1], dv[:, k0:k1] = bwd(q[:, q0:q1], k[:, k0:k1], v[:, k0:k1], dout[:, q0:q1],
+                                                       causal, scale, window=window)
+    return dq, dk, dv

@@ -42,6 +42,11 @@
  *       dQ = scale * dS K
  *       dK = scale * dS^T Q
  *
+ * Masks: causal, and an optional sliding window, with query rows placed at
+ * key positions qpos (see visible()); rectangular n_q != n_k shapes align the
+ * rows to the end of the key sequence.  Variable-length batches are handled
+ * by the Python wrapper, one sequence at a time.
+ *
  * Layout: every array is a batch of G independent heads, row-major
  * [G, rows, d] (lse: [G, rows]).  Rows are processed one at a time, so the
  * N x N score matrix is never held in memory; OpenMP spreads rows over cores.
@@ -62,8 +67,29 @@ static double dot(const double* a, const double* b, int64_t d) {
     return s;
 }
 
-/* Key j is visible to a query at sequence position pos iff (not causal) or j <= pos. */
-static int visible(int causal, int64_t j, int64_t pos) { return !causal || j <= pos; }
+/*
+ * Which keys a query row sees.  The row sits at key position pos (for equal
+ * query and key lengths pos is the row index; for n_q != n_k the rows are
+ * aligned to the end of the key sequence, pos = i + n_k - n_q).  Key j is
+ * visible iff
+ *     (causal: j <= pos)                    -- the causal call of the snabindia
+ *                                              page's chapter 1 skips the upper triangle
+ *     and (wl < 0 or j >= pos - wl)         -- sliding window to the left
+ *     and (wr < 0 or j <= pos + wr)         -- sliding window to the right
+ * (a local window of the kind the yunthe article's hybrid local/global block
+ * uses).  wl = wr = -1 means no window.
+ */
+typedef struct {
+    int causal;
+    int64_t wl, wr;
+} mask_t;
+
+static int visible(mask_t mk, int64_t j, int64_t pos) {
+    if (mk.causal && j > pos) return 0;
+    if (mk.wl >= 0 && j < pos - mk.wl) return 0;
+    if (mk.wr >= 0 && j > pos + mk.wr) return 0;
+    return 1;
+}
 
 /*
  * Forward, three passes per query row.
@@ -73,8 +99,9 @@ static int visible(int causal, int64_t j, int64_t pos) { return !causal || j <= 
  */
 int oracle_attn_fwd(int64_t G, int64_t nq, int64_t nk, int64_t d,
                     const double* q, const double* k, const double* v,
-                    const int64_t* qpos, int causal, double scale,
+                    const int64_t* qpos, int causal, int64_t wl, int64_t wr, double scale,
                     double* o, double* lse) {
+    const mask_t mk = {causal, wl, wr};
     int failed = 0;
 #pragma omp parallel
     {
@@ -93,7 +120,7 @@ int oracle_attn_fwd(int64_t G, int64_t nq, int64_t nk, int64_t d,
             double* oi = o + (g * nq + i) * d;
             /* pass 1: scores */
             for (int64_t j = 0; j < nk; ++j)
-                s[j] = visible(causal, j, qpos[i]) ? scale * dot(qi, kg + j * d, d) : -INFINITY;
+                s[j] = visible(mk, j, qpos[i]) ? scale * dot(qi, kg + j * d, d) : -INFINITY;
             /* pass 2: max-shifted softmax */
             double m = -INFINITY;
             for (int64_t j = 0; j < nk; ++j) if (s[j] > m) m = s[j];
@@ -127,8 +154,9 @@ int oracle_attn_fwd(int64_t G, int64_t nq, int64_t nk, int64_t d,
  */
 int oracle_attn_fwd_online(int64_t G, int64_t nq, int64_t nk, int64_t d,
                            const double* q, const double* k, const double* v,
-                           const int64_t* qpos, int causal, double scale, int64_t block,
-                           double* o, double* lse) {
+                           const int64_t* qpos, int causal, int64_t wl, int64_t wr, double scale,
+                           int64_t block, double* o, double* lse) {
+    const mask_t mk = {causal, wl, wr};
     if (block < 1) return -2;
     int failed = 0;
 #pragma omp parallel
@@ -154,7 +182,7 @@ int oracle_attn_fwd_online(int64_t G, int64_t nq, int64_t nk, int64_t d,
                 double m_local = -INFINITY;
                 for (int64_t t = 0; t < nb; ++t) {
                     int64_t j = j0 + t;
-                    s[t] = visible(causal, j, qpos[i]) ? scale * dot(qi, kg + j * d, d) : -INFINITY;
+                    s[t] = visible(mk, j, qpos[i]) ? scale * dot(qi, kg + j * d, d) : -INFINITY;
                     if (s[t] > m_local) m_local = s[t];
                 }
                 if (m_local == -INFINITY) continue; /* nothing visible in this block */
@@ -189,38 +217,42 @@ int oracle_attn_fwd_online(int64_t G, int64_t nq, int64_t nk, int64_t d,
 }
 
 /*
- * Backward.  q, k, v, dout: [G, n, d].  Outputs only the requested rows:
- *   dq: [G, nrows, d] for query rows rows[0..nrows)   (rows == NULL: all n rows)
- *   dk, dv: [G, nkeys, d] for key rows keys[0..nkeys) (keys == NULL: all n keys)
+ * Backward.  q, dout: [G, nq, d]; k, v: [G, nk, d]; qpos: [nq] key position
+ * of each query row (see visible()).  Outputs only the requested rows:
+ *   dq: [G, nrows, d] for query rows rows[0..nrows)   (rows == NULL: all nq rows)
+ *   dk, dv: [G, nkeys, d] for key rows keys[0..nkeys) (keys == NULL: all nk keys)
  * Row statistics m_i, l_i and D_i are computed for every query row that
  * contributes (all rows when any dk/dv is requested), then
  *   dq_i = scale * sum_j P_ij (dP_ij - D_i) k_j
  *   dv_j = sum_i P_ij dO_i
  *   dk_j = scale * sum_i P_ij (dP_ij - D_i) q_i
- * with P_ij = exp(S_ij - m_i) / l_i and dP_ij = <dO_i, v_j>.
- * Returns 0, -1 on allocation failure.
+ * with P_ij = exp(S_ij - m_i) / l_i over visible keys (0 elsewhere) and
+ * dP_ij = <dO_i, v_j>.  A row that sees no key has P = 0 and contributes
+ * nothing.  Returns 0, -1 on allocation failure.
  */
-int oracle_attn_bwd(int64_t G, int64_t n, int64_t d,
+int oracle_attn_bwd(int64_t G, int64_t nq, int64_t nk, int64_t d,
                     const double* q, const double* k, const double* v, const double* dout,
-                    int causal, double scale,
+                    const int64_t* qpos, int causal, int64_t wl, int64_t wr, double scale,
                     const int64_t* rows, int64_t nrows, double* dq,
                     const int64_t* keys, int64_t nkeys, double* dk, double* dv) {
-    if (rows == NULL) nrows = n;
-    if (keys == NULL) nkeys = n;
+    const mask_t mk = {causal, wl, wr};
+    if (rows == NULL) nrows = nq;
+    if (keys == NULL) nkeys = nk;
     /* Which query rows need statistics: all of them if any key gradient is asked for. */
     int need_all = nkeys > 0;
-    int64_t nstat = need_all ? n : nrows;
-    double* m = (double*)malloc(sizeof(double) * (size_t)(G * n > 0 ? G * n : 1));
-    double* l = (double*)malloc(sizeof(double) * (size_t)(G * n > 0 ? G * n : 1));
-    double* D = (double*)malloc(sizeof(double) * (size_t)(G * n > 0 ? G * n : 1));
+    int64_t nstat = need_all ? nq : nrows;
+    size_t ns = (size_t)(G * nq > 0 ? G * nq : 1);
+    double* m = (double*)malloc(sizeof(double) * ns);
+    double* l = (double*)malloc(sizeof(double) * ns);
+    double* D = (double*)malloc(sizeof(double) * ns);
     if (!m || !l || !D) { free(m); free(l); free(D); return -1; }
     int failed = 0;
 
     /* Phase 1: per query row, the softmax statistics and D_i = sum_j P_ij dP_ij. */
 #pragma omp parallel
     {
-        double* s = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
-        double* dp = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        double* s = (double*)malloc(sizeof(double) * (size_t)(nk > 0 ? nk : 1));
+        double* dp = (double*)malloc(sizeof(double) * (size_t)(nk > 0 ? nk : 1));
         if (!s || !dp) {
 #pragma omp atomic write
             failed = 1;
@@ -230,29 +262,30 @@ int oracle_attn_bwd(int64_t G, int64_t n, int64_t d,
             if (!s || !dp) continue;
             int64_t g = r / nstat, ii = r % nstat;
             int64_t i = (need_all || rows == NULL) ? ii : rows[ii];
-            const double* qi = q + (g * n + i) * d;
-            const double* doi = dout + (g * n + i) * d;
-            const double* kg = k + g * n * d;
-            const double* vg = v + g * n * d;
+            const double* qi = q + (g * nq + i) * d;
+            const double* doi = dout + (g * nq + i) * d;
+            const double* kg = k + g * nk * d;
+            const double* vg = v + g * nk * d;
             double mi = -INFINITY;
-            for (int64_t j = 0; j < n; ++j) {
-                s[j] = visible(causal, j, i) ? scale * dot(qi, kg + j * d, d) : -INFINITY;
+            for (int64_t j = 0; j < nk; ++j) {
+                s[j] = visible(mk, j, qpos[i]) ? scale * dot(qi, kg + j * d, d) : -INFINITY;
                 if (s[j] > mi) mi = s[j];
             }
-            double li = 0.0;
-            for (int64_t j = 0; j < n; ++j) {
-                s[j] = (s[j] == -INFINITY) ? 0.0 : exp(s[j] - mi);
-                li += s[j];
+            double li = 0.0, Di = 0.0;
+            if (mi != -INFINITY) {
+                for (int64_t j = 0; j < nk; ++j) {
+                    s[j] = (s[j] == -INFINITY) ? 0.0 : exp(s[j] - mi);
+                    li += s[j];
+                }
+                for (int64_t j = 0; j < nk; ++j) {
+                    s[j] /= li; /* P_ij */
+                    dp[j] = (s[j] == 0.0) ? 0.0 : dot(doi, vg + j * d, d);
+                    Di += s[j] * dp[j];
+                }
             }
-            double Di = 0.0;
-            for (int64_t j = 0; j < n; ++j) {
-                s[j] /= li; /* P_ij */
-                dp[j] = (s[j] == 0.0) ? 0.0 : dot(doi, vg + j * d, d);
-                Di += s[j] * dp[j];
-            }
-            m[g * n + i] = mi;
-            l[g * n + i] = li;
-            D[g * n + i] = Di;
+            m[g * nq + i] = mi;
+            l[g * nq + i] = li;
+            D[g * nq + i] = Di;
         }
         free(s);
         free(dp);
@@ -264,16 +297,17 @@ int oracle_attn_bwd(int64_t G, int64_t n, int64_t d,
     for (int64_t r = 0; r < G * nrows; ++r) {
         int64_t g = r / nrows, ii = r % nrows;
         int64_t i = rows ? rows[ii] : ii;
-        const double* qi = q + (g * n + i) * d;
-        const double* doi = dout + (g * n + i) * d;
-        const double* kg = k + g * n * d;
-        const double* vg = v + g * n * d;
+        const double* qi = q + (g * nq + i) * d;
+        const double* doi = dout + (g * nq + i) * d;
+        const double* kg = k + g * nk * d;
+        const double* vg = v + g * nk * d;
         double* dqi = dq + (g * nrows + ii) * d;
         for (int64_t c = 0; c < d; ++c) dqi[c] = 0.0;
-        for (int64_t j = 0; j < n; ++j) {
-            if (!visible(causal, j, i)) continue;
-            double p = exp(scale * dot(qi, kg + j * d, d) - m[g * n + i]) / l[g * n + i];
-            double ds = p * (dot(doi, vg + j * d, d) - D[g * n + i]);
+        if (m[g * nq + i] == -INFINITY) continue; /* the row sees no key */
+        for (int64_t j = 0; j < nk; ++j) {
+            if (!visible(mk, j, qpos[i])) continue;
+            double p = exp(scale * dot(qi, kg + j * d, d) - m[g * nq + i]) / l[g * nq + i];
+            double ds = p * (dot(doi, vg + j * d, d) - D[g * nq + i]);
             for (int64_t c = 0; c < d; ++c) dqi[c] += scale * ds * kg[j * d + c];
         }
     }
@@ -283,17 +317,17 @@ int oracle_attn_bwd(int64_t G, int64_t n, int64_t d,
     for (int64_t r = 0; r < G * nkeys; ++r) {
         int64_t g = r / nkeys, jj = r % nkeys;
         int64_t j = keys ? keys[jj] : jj;
-        const double* kj = k + (g * n + j) * d;
-        const double* vj = v + (g * n + j) * d;
+        const double* kj = k + (g * nk + j) * d;
+        const double* vj = v + (g * nk + j) * d;
         double* dkj = dk + (g * nkeys + jj) * d;
         double* dvj = dv + (g * nkeys + jj) * d;
         for (int64_t c = 0; c < d; ++c) { dkj[c] = 0.0; dvj[c] = 0.0; }
-        for (int64_t i = 0; i < n; ++i) {
-            if (!visible(causal, j, i)) continue;
-            const double* qi = q + (g * n + i) * d;
-            const double* doi = dout + (g * n + i) * d;
-            double p = exp(scale * dot(qi, kj, d) - m[g * n + i]) / l[g * n + i];
-            double ds = p * (dot(doi, vj, d) - D[g * n + i]);
+        for (int64_t i = 0; i < nq; ++i) {
+            if (!visible(mk, j, qpos[i])) continue;
+            const double* qi = q + (g * nq + i) * d;
+            const double* doi = dout + (g * nq + i) * d;
+            double p = exp(scale * dot(qi, kj, d) - m[g * nq + i]) / l[g * nq + i];
+            double ds = p * (dot(doi, vj, d) - D[g * nq + i]);
             for (int64_t c = 0; c < d; ++c) {
                 dvj[c] += p * doi[c];
                 dkj[c] += scale * ds * qi[c];

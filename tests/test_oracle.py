@@ -29,49 +29,68 @@ def rand(*shape, scale=1.0, rng=RNG):
 # independent scalar brute force (pure Python, exact summation with math.fsum)
 # ----------------------------------------------------------------------------
 
-def brute_fwd(q, k, v, causal, scale):
-    """O and lse of one head by the definition, scalar Python, math.fsum sums."""
+def vis(j, pos, causal, window):
+    """Key j visible to a row at key position pos (independent restatement of the mask)."""
+    wl, wr = window
+    return (not causal or j <= pos) and (wl < 0 or j >= pos - wl) and (wr < 0 or j <= pos + wr)
+
+
+def brute_fwd(q, k, v, causal, scale, window=(-1, -1)):
+    """O and lse of one head by the definition, scalar Python, math.fsum sums.
+
+    Rows are aligned to the end of the keys (row i at key position i + nk - nq).
+    A row with no visible key gives O = 0, lse = -inf.
+    """
     n, d = len(q), len(q[0])
     nk = len(k)
     O, L = [], []
     for i in range(n):
-        vis = [j for j in range(nk) if (not causal) or j <= i]
-        s = {j: scale * math.fsum(q[i][c] * k[j][c] for c in range(d)) for j in vis}
+        pos = i + nk - n
+        vis_j = [j for j in range(nk) if vis(j, pos, causal, window)]
+        if not vis_j:
+            O.append([0.0] * d)
+            L.append(-math.inf)
+            continue
+        s = {j: scale * math.fsum(q[i][c] * k[j][c] for c in range(d)) for j in vis_j}
         m = max(s.values())
-        e = {j: math.exp(s[j] - m) for j in vis}
+        e = {j: math.exp(s[j] - m) for j in vis_j}
         l = math.fsum(e.values())
-        O.append([math.fsum(e[j] / l * v[j][c] for j in vis) for c in range(d)])
+        O.append([math.fsum(e[j] / l * v[j][c] for j in vis_j) for c in range(d)])
         L.append(m + math.log(l))
     return np.array(O), np.array(L)
 
 
-def brute_bwd_jacobian(q, k, v, do, causal, scale):
+def brute_bwd_jacobian(q, k, v, do, causal, scale, window=(-1, -1)):
     """Gradients through the explicit softmax Jacobian dP_ij/dS_ij' = P_ij (delta_jj' - P_ij').
 
     A different route from the oracle's D-trick: it builds the full per-row
     Jacobian (the O(n^2) formulation) and contracts it, scalar Python.
     """
     n, d = len(q), len(q[0])
+    nk = len(k)
     dq = [[0.0] * d for _ in range(n)]
-    dk = [[0.0] * d for _ in range(n)]
-    dv = [[0.0] * d for _ in range(n)]
+    dk = [[0.0] * d for _ in range(nk)]
+    dv = [[0.0] * d for _ in range(nk)]
     for i in range(n):
-        vis = [j for j in range(n) if (not causal) or j <= i]
-        s = {j: scale * math.fsum(q[i][c] * k[j][c] for c in range(d)) for j in vis}
+        pos = i + nk - n
+        vis_j = [j for j in range(nk) if vis(j, pos, causal, window)]
+        if not vis_j:
+            continue
+        s = {j: scale * math.fsum(q[i][c] * k[j][c] for c in range(d)) for j in vis_j}
         m = max(s.values())
-        e = {j: math.exp(s[j] - m) for j in vis}
+        e = {j: math.exp(s[j] - m) for j in vis_j}
         l = math.fsum(e.values())
-        P = {j: e[j] / l for j in vis}
+        P = {j: e[j] / l for j in vis_j}
         # dL/dP_ij = <dO_i, v_j>; dL/dv_j += P_ij dO_i
-        gP = {j: math.fsum(do[i][c] * v[j][c] for c in range(d)) for j in vis}
-        for j in vis:
+        gP = {j: math.fsum(do[i][c] * v[j][c] for c in range(d)) for j in vis_j}
+        for j in vis_j:
             for c in range(d):
                 dv[j][c] += P[j] * do[i][c]
         # dL/dS_ij = sum_j' gP_ij' * P_ij' (delta_j'j - P_ij)
         gS = {}
-        for j in vis:
-            gS[j] = math.fsum(gP[jp] * P[jp] * ((1.0 if jp == j else 0.0) - P[j]) for jp in vis)
-        for j in vis:
+        for j in vis_j:
+            gS[j] = math.fsum(gP[jp] * P[jp] * ((1.0 if jp == j else 0.0) - P[j]) for jp in vis_j)
+        for j in vis_j:
             for c in range(d):
                 dq[i][c] += scale * gS[j] * k[j][c]
                 dk[j][c] += scale * gS[j] * q[i][c]
@@ -96,10 +115,15 @@ def decimal_fwd(q, k, v, causal, scale, digits=50):
 
 
 def relerr(a, b):
-    """max|a - b| / max|b|; infinite when either side holds a NaN/inf or the shapes differ."""
+    """max|a - b| / max|b| over finite entries; infinite when the shapes differ, a
+    NaN appears, or the two sides are not infinite in exactly the same places."""
     a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
-    if a.shape != b.shape or not (np.isfinite(a).all() and np.isfinite(b).all()):
+    if a.shape != b.shape or np.isnan(a).any() or np.isnan(b).any():
         return math.inf
+    fa, fb = np.isfinite(a), np.isfinite(b)
+    if not np.array_equal(fa, fb) or not np.array_equal(a[~fa], b[~fb]):
+        return math.inf
+    a, b = a[fa], b[fb]
     if a.size == 0:
         return 0.0
     return float(np.max(np.abs(a - b)) / max(1e-300, np.max(np.abs(b))))
@@ -130,6 +154,24 @@ def pin_battery(lib):
                 oo, ll = lib.fwd_online(q, k, v, causal, scale, blk)
                 if relerr(oo, o) > 1e-12 or relerr(ll, lse) > 1e-12:
                     fails.append("online blk=%d n=%d causal=%d" % (blk, n, causal))
+        # rectangular shapes (rows aligned to the end of the keys) and sliding windows
+        for (nq, nk, window) in ((3, 7, (-1, -1)), (7, 3, (-1, -1)), (6, 6, (2, -1)), (6, 6, (1, 1)),
+                                 (4, 9, (3, 0)), (8, 5, (-1, 2))):
+            d = 3
+            q, do = rng.standard_normal((nq, d)), rng.standard_normal((nq, d))
+            k, v = rng.standard_normal((nk, d)), rng.standard_normal((nk, d))
+            o, lse = lib.fwd(q, k, v, causal, 0.8, window=window)
+            bo, bl = brute_fwd(q.tolist(), k.tolist(), v.tolist(), causal, 0.8, window)
+            if relerr(o[0], bo) > 1e-13 or relerr(lse[0], bl) > 1e-13:
+                fails.append("brute fwd %dx%d window=%s causal=%d" % (nq, nk, window, causal))
+            dq, dk, dv = lib.bwd(q, k, v, do, causal, 0.8, window=window)
+            bq, bk, bv = brute_bwd_jacobian(q.tolist(), k.tolist(), v.tolist(), do.tolist(), causal, 0.8, window)
+            for name, a, b in (("dq", dq[0], bq), ("dk", dk[0], bk), ("dv", dv[0], bv)):
+                if relerr(a, b) > 1e-12:
+                    fails.append("brute %s %dx%d window=%s causal=%d" % (name, nq, nk, window, causal))
+            oo, ll = lib.fwd_online(q, k, v, causal, 0.8, 2, window=window)
+            if relerr(oo, o) > 1e-12 or relerr(ll, lse) > 1e-12:
+                fails.append("online %dx%d window=%s causal=%d" % (nq, nk, window, causal))
     return fails
 
 
@@ -333,17 +375,20 @@ def test_row_and_key_selection(causal):
 # ----------------------------------------------------------------------------
 
 MUTANTS = {
-    "causal_excludes_diagonal": ("return !causal || j <= pos;", "return !causal || j < pos;"),
-    "causal_flipped": ("return !causal || j <= pos;", "return !causal || j >= pos;"),
+    "causal_excludes_diagonal": ("if (mk.causal && j > pos) return 0;", "if (mk.causal && j >= pos) return 0;"),
+    "causal_flipped": ("if (mk.causal && j > pos) return 0;", "if (mk.causal && j < pos) return 0;"),
     "lse_drops_max": ("lse[g * nq + i] = m + log(l);\n        }\n        free(s);",
                       "lse[g * nq + i] = log(l);\n        }\n        free(s);"),
     "unnormalised_weights": ("for (int64_t j = 0; j < nk; ++j) s[j] /= l;", ""),
-    "scale_dropped_in_scores": ("s[j] = visible(causal, j, qpos[i]) ? scale * dot(qi, kg + j * d, d) : -INFINITY;",
-                                "s[j] = visible(causal, j, qpos[i]) ? dot(qi, kg + j * d, d) : -INFINITY;"),
+    "scale_dropped_in_scores": ("s[j] = visible(mk, j, qpos[i]) ? scale * dot(qi, kg + j * d, d) : -INFINITY;\n            /* pass 2",
+                                "s[j] = visible(mk, j, qpos[i]) ? dot(qi, kg + j * d, d) : -INFINITY;\n            /* pass 2"),
     "online_no_output_rescale": ("for (int64_t c = 0; c < d; ++c) acc[c] *= alpha;", ""),
     "online_no_sum_rescale": ("l *= alpha;", ""),
-    "ds_sign": ("double ds = p * (dot(doi, vg + j * d, d) - D[g * n + i]);",
-                "double ds = p * (D[g * n + i] - dot(doi, vg + j * d, d));"),
+    "window_left_off_by_one": ("if (mk.wl >= 0 && j < pos - mk.wl) return 0;", "if (mk.wl >= 0 && j <= pos - mk.wl) return 0;"),
+    "window_right_ignored": ("if (mk.wr >= 0 && j > pos + mk.wr) return 0;", ""),
+    "bwd_ignores_qpos": ("if (!visible(mk, j, qpos[i])) continue;\n            const double* qi", "if (!visible(mk, j, i)) continue;\n            const double* qi"),
+    "ds_sign": ("double ds = p * (dot(doi, vg + j * d, d) - D[g * nq + i]);",
+                "double ds = p * (D[g * nq + i] - dot(doi, vg + j * d, d));"),
     "D_missing_P": ("Di += s[j] * dp[j];", "Di += dp[j];"),
     "dk_transposed_operand": ("dkj[c] += scale * ds * qi[c];", "dkj[c] += scale * ds * kj[c];"),
     "dq_missing_scale": ("dqi[c] += scale * ds * kg[j * d + c];", "dqi[c] += ds * kg[j * d + c];"),
@@ -362,3 +407,93 @@ def test_planted_mistake_is_caught(name, tmp_path):
     path.write_text(mutated)
     lib = oracle.OracleLib(oracle.compile_source(str(path), str(tmp_path / ("lib%s.so" % name))))
     assert pin_battery(lib) != [], "planted mistake %s passed every pin" % name
+
+
+# ----------------------------------------------------------------------------
+# rectangular shapes, sliding windows, variable-length batches
+# ----------------------------------------------------------------------------
+
+def _mask_matrix(nq, nk, causal, window):
+    pos = np.arange(nq)[:, None] + (nk - nq)
+    j = np.arange(nk)[None, :]
+    m = np.ones((nq, nk), bool)
+    if causal:
+        m &= j <= pos
+    if window[0] >= 0:
+        m &= j >= pos - window[0]
+    if window[1] >= 0:
+        m &= j <= pos + window[1]
+    return m
+
+
+def _torch_masked(q, k, v, do, mask, scale):
+    tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
+    tm = torch.tensor(mask)
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=tm, scale=scale)
+    o.backward(torch.tensor(do, dtype=torch.float64))
+    s = scale * (tq.detach() @ tk.detach().transpose(-1, -2))
+    lse = torch.logsumexp(s.masked_fill(~tm, float("-inf")), -1)
+    return o.detach().numpy(), lse.numpy(), tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+@pytest.mark.parametrize("nq,nk,causal,window", [
+    (96, 160, True, (-1, -1)), (160, 160, False, (31, 17)), (128, 128, True, (40, -1)),
+    (70, 200, False, (-1, 0)), (200, 200, True, (63, 0)),
+])
+def test_rectangular_and_window_against_torch_masked(nq, nk, causal, window):
+    G, d, scale = 2, 16, 0.3
+    q, do = rand(G, nq, d), rand(G, nq, d)
+    k, v = rand(G, nk, d), rand(G, nk, d)
+    mask = _mask_matrix(nq, nk, causal, window)
+    assert mask.any(axis=1).all()  # every row sees a key (torch gives NaN otherwise)
+    to, tl, tdq, tdk, tdv = _torch_masked(q, k, v, do, mask, scale)
+    o, l = oracle.fwd(q, k, v, causal, scale, window=window)
+    assert relerr(o, to) <= 1e-12 and relerr(l, tl) <= 1e-12
+    dq, dk, dv = oracle.bwd(q, k, v, do, causal, scale, window=window)
+    assert relerr(dq, tdq) <= 1e-11 and relerr(dk, tdk) <= 1e-11 and relerr(dv, tdv) <= 1e-11
+
+
+def test_rows_without_keys_in_rectangular_causal():
+    # more queries than keys: the first nq - nk rows see no key at all
+    q, k, v, do = rand(1, 9, 4), rand(1, 5, 4), rand(1, 5, 4), rand(1, 9, 4)
+    o, l = oracle.fwd(q, k, v, True, 0.5)
+    assert np.all(o[0, :4] == 0.0) and np.all(l[0, :4] == -np.inf) and np.isfinite(l[0, 4:]).all()
+    dq, dk, dv = oracle.bwd(q, k, v, do, True, 0.5)
+    assert np.all(dq[0, :4] == 0.0)
+    bq, bk, bv = brute_bwd_jacobian(q[0].tolist(), k[0].tolist(), v[0].tolist(), do[0].tolist(), True, 0.5)
+    assert relerr(dq[0], bq) <= 1e-12 and relerr(dk[0], bk) <= 1e-12 and relerr(dv[0], bv) <= 1e-12
+
+
+def test_window_q_zero_gives_window_mean():
+    n, d, wl = 50, 3, 7
+    q = np.zeros((1, n, d))
+    k, v = rand(1, n, d), rand(1, n, d)
+    o, l = oracle.fwd(q, k, v, True, 0.4, window=(wl, -1))
+    for i in range(n):
+        lo = max(0, i - wl)
+        assert np.max(np.abs(o[0, i] - v[0, lo:i + 1].mean(0))) <= 1e-13
+        assert abs(l[0, i] - math.log(i + 1 - lo)) <= 1e-13
+
+
+@pytest.mark.parametrize("causal,window", [(False, (-1, -1)), (True, (-1, -1)), (True, (5, 0))])
+def test_varlen_against_block_diagonal_torch(causal, window):
+    H, d, scale = 3, 8, 0.35
+    lq = [5, 0, 17, 1, 9]
+    lk = [5, 3, 20, 1, 12]
+    cu_q, cu_k = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    tq, tk = int(cu_q[-1]), int(cu_k[-1])
+    q, do = rand(H, tq, d), rand(H, tq, d)
+    k, v = rand(H, tk, d), rand(H, tk, d)
+    o, l = oracle.fwd_varlen(q, k, v, cu_q, cu_k, causal, scale, window)
+    dq, dk, dv = oracle.bwd_varlen(q, k, v, do, cu_q, cu_k, causal, scale, window)
+    # one big masked attention over the packed rows: block diagonal x per-sequence mask
+    mask = np.zeros((tq, tk), bool)
+    for b in range(len(lq)):
+        mask[cu_q[b]:cu_q[b + 1], cu_k[b]:cu_k[b + 1]] = _mask_matrix(lq[b], lk[b], causal, window)
+    seen = mask.any(axis=1)
+    to, tl, tdq, tdk, tdv = _torch_masked(q, k, v, do, mask, scale)
+    assert relerr(o[:, seen], to[:, seen]) <= 1e-12 and relerr(l[:, seen], tl[:, seen]) <= 1e-12
+    assert relerr(dq[:, seen], tdq[:, seen]) <= 1e-11
+    assert relerr(dk, np.where(np.isnan(tdk), 0.0, tdk)) <= 1e-11
+    assert relerr(dv, np.where(np.isnan(tdv), 0.0, tdv)) <= 1e-11
+    assert np.all(o[:, ~seen] == 0.0) and np.all(l[:, ~seen] == -np.inf)
