@@ -102,6 +102,59 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int B, int H, int N, int d, int causal, float scale, int dtype,
              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Packed variable-length batches, rectangular shapes and sliding windows.
+ *
+ * Layout.  A call holds `batch` independent sequences packed along the row
+ * axis: q, o are [H, total_q, d], k, v are [H, total_k, d], lse is
+ * [H, total_q] fp32.  Sequence b owns query rows cu_seqlens_q[b] ..
+ * cu_seqlens_q[b+1]-1 and key rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of
+ * every head.  cu_seqlens_q and cu_seqlens_k are DEVICE arrays of batch+1
+ * int32 offsets (0 first, non-decreasing, total last); the kernels clamp every
+ * offset to [0, total] and treat a decreasing pair as an empty sequence, so
+ * bad offsets give wrong rows but never an out-of-bounds access.  This is the
+ * padding-free form of the variable-length masking the yunthe article's
+ * section 三.3 describes: no [B,1,N,N] mask is ever built.
+ *
+ * Rectangular sequences.  A sequence may have nq != nk; its query rows are
+ * aligned to the end of its keys: row i sits at key position
+ * pos = i + nk - nq (the prefill-with-cache shape).
+ *
+ * Visible keys.  Key j is visible to row i iff (causal == 0 or j <= pos) and
+ * (window_left < 0 or j >= pos - window_left) and (window_right < 0 or
+ * j <= pos + window_right): a sliding local window of the kind the yunthe
+ * article's hybrid local/global attention uses (section 三.1), applied
+ * exactly; key tiles outside every row's window are skipped, tiles inside
+ * every row's window run unmasked.  A row that sees no key gets O = 0 and
+ * lse = -inf.  window_left, window_right >= -1 (-1: unbounded).
+ *
+ * max_seqlen_q (and max_seqlen_k for the backward) bound the grid: rows of a
+ * longer sequence past that length are not computed and their outputs are
+ * left unwritten.  Other arguments, memory, errors: as for attn_fwd /
+ * attn_bwd (empty calls -- batch*H == 0, total_q == 0 or max_seqlen_q == 0
+ * for the forward -- return ATTN_OK without examining pointers).
+ */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int H,
+                    int total_q, int total_k, int max_seqlen_q, int d, int causal,
+                    int window_left, int window_right, float scale, int dtype, void* stream);
+
+/* Workspace bytes of attn_bwd_varlen: one fp32 per query row (H * total_q),
+ * rounded up to 256; (size_t)-1 for negative sizes. */
+size_t attn_bwd_varlen_workspace_bytes(int H, int total_q);
+
+/*
+ * Backward of attn_fwd_varlen by recomputation.  dq is [H, total_q, d]; dk,
+ * dv are [H, total_k, d]; o and lse come from attn_fwd_varlen with the same
+ * arguments.  Keys that no query row sees get zero gradients.
+ */
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int batch, int H,
+                    int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d, int causal,
+                    int window_left, int window_right, float scale, int dtype,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* A static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_string(int status);
 

@@ -22,7 +22,8 @@ STATUS = {
     0: "ATTN_OK", 1: "ATTN_E_NULL", 2: "ATTN_E_SHAPE", 3: "ATTN_E_UNSUPPORTED",
     4: "ATTN_E_ALIGN", 5: "ATTN_E_ALIAS", 6: "ATTN_E_WORKSPACE", 7: "ATTN_E_HIP",
 }
-EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_string")
+EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_string",
+           "attn_fwd_varlen", "attn_bwd_varlen", "attn_bwd_varlen_workspace_bytes")
 
 _lib = None
 
@@ -50,6 +51,13 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd.restype = i
         L.attn_status_string.argtypes = [i]
         L.attn_status_string.restype = ctypes.c_char_p
+        L.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, vp]
+        L.attn_fwd_varlen.restype = i
+        L.attn_bwd_varlen_workspace_bytes.argtypes = [i, i]
+        L.attn_bwd_varlen_workspace_bytes.restype = sz
+        L.attn_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i,
+                                      f, i, vp, sz, vp]
+        L.attn_bwd_varlen.restype = i
         _lib = L
     return _lib
 
@@ -72,6 +80,24 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal, scale, dtype
              workspace, workspace_bytes, stream) -> int:
     return lib().attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, int(causal),
                           float(scale), dtype, workspace, workspace_bytes, stream)
+
+
+def attn_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, batch, H, total_q, total_k, max_q, d, causal,
+                    window_left, window_right, scale, dtype, stream) -> int:
+    return lib().attn_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, batch, H, total_q, total_k, max_q, d,
+                                 int(causal), window_left, window_right, float(scale), dtype, stream)
+
+
+def attn_bwd_varlen_workspace_bytes(H, total_q) -> int:
+    return int(lib().attn_bwd_varlen_workspace_bytes(H, total_q))
+
+
+def attn_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, cu_q, cu_k, batch, H, total_q, total_k, max_q, max_k,
+                    d, causal, window_left, window_right, scale, dtype, workspace, workspace_bytes,
+                    stream) -> int:
+    return lib().attn_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, cu_q, cu_k, batch, H, total_q, total_k,
+                                 max_q, max_k, d, int(causal), window_left, window_right, float(scale), dtype,
+                                 workspace, workspace_bytes, stream)
 
 
 def _check(status: int):
@@ -139,4 +165,63 @@ def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
                     lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
                     causal, scale, _dtype_code(q), workspace.data_ptr(), workspace.numel(),
                     _stream_handle(q.device)))
+    return dq, dk, dv
+
+
+def _packed(q, k, v):
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("packed tensors are [H, total, d]")
+    H, tq, d = (int(x) for x in q.shape)
+    if k.shape[0] != H or k.shape[2] != d or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share heads, d and dtype")
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    return H, tq, int(k.shape[1]), d
+
+
+def _cu(cu, device):
+    import torch
+    if not (cu.dtype == torch.int32 and cu.device == device and cu.is_contiguous()):
+        raise ValueError("cu_seqlens must be contiguous int32 tensors on the tensors' device")
+    return int(cu.numel()) - 1
+
+
+def fwd_varlen(q, k, v, cu_q, cu_k, max_seqlen_q: int, causal: bool = False, scale: float | None = None,
+               window=(-1, -1), o=None, lse=None):
+    """Packed variable-length forward: q [H, total_q, d], k, v [H, total_k, d]."""
+    import torch
+    H, tq, tk, d = _packed(q, k, v)
+    batch = _cu(cu_q, q.device)
+    if _cu(cu_k, q.device) != batch:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k describe different batch sizes")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((H, tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                           cu_q.data_ptr(), cu_k.data_ptr(), batch, H, tq, tk, int(max_seqlen_q), d, causal,
+                           int(window[0]), int(window[1]), scale, _dtype_code(q), _stream_handle(q.device)))
+    return o, lse
+
+
+def bwd_varlen(q, k, v, o, dout, lse, cu_q, cu_k, max_seqlen_q: int, max_seqlen_k: int, causal: bool = False,
+               scale: float | None = None, window=(-1, -1), dq=None, dk=None, dv=None, workspace=None):
+    """Backward of fwd_varlen: returns dq [H, total_q, d], dk, dv [H, total_k, d]."""
+    import torch
+    H, tq, tk, d = _packed(q, k, v)
+    batch = _cu(cu_q, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = attn_bwd_varlen_workspace_bytes(H, tq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(attn_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                           lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cu_q.data_ptr(),
+                           cu_k.data_ptr(), batch, H, tq, tk, int(max_seqlen_q), int(max_seqlen_k), d, causal,
+                           int(window[0]), int(window[1]), scale, _dtype_code(q), workspace.data_ptr(),
+                           workspace.numel(), _stream_handle(q.device)))
     return dq, dk, dv

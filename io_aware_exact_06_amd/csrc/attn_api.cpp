@@ -76,7 +76,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv) || overlap(rl, rq) || overlap(rl, rk) ||
         overlap(rl, rv) || overlap(ro, rl))
         return ATTN_E_ALIAS;
-    attn::FwdParams p{q, k, v, o, lse, B, H, N, d, causal, dtype, scale, stream};
+    attn::SeqLayout L{0, B, H, N, nullptr, nullptr, N, N, -1, causal ? 0 : -1};
+    attn::FwdParams p{q, k, v, o, lse, L, N, d, dtype, scale, stream};
     return attn::launch_fwd(p) == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 
@@ -84,7 +85,7 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N, int d) {
     if (B < 0 || H < 0 || N < 0 || d < 0) return (size_t)-1;
     if ((int64_t)B * H * N == 0) return 0;
     (void)d;
-    return attn::bwd_workspace_bytes(B, H, N);
+    return attn::bwd_workspace_bytes_rows((int64_t)B * H * N);
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -100,7 +101,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     for (const void* p : a16)
         if (!aligned(p, 16)) return ATTN_E_ALIGN;
     if (!aligned(lse, 4)) return ATTN_E_ALIGN;
-    const size_t ws_need = attn::bwd_workspace_bytes(B, H, N);
+    const size_t ws_need = attn::bwd_workspace_bytes_rows(rows);
     if (workspace_bytes < ws_need) return ATTN_E_WORKSPACE;
     const size_t tb = (size_t)elems * 2, lb = (size_t)rows * 4;
     const Range ins[] = {range_of(q, tb), range_of(k, tb), range_of(v, tb), range_of(o, tb),
@@ -113,8 +114,99 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
         for (int j = i + 1; j < 4; ++j)
             if (overlap(outs[i], outs[j])) return j == 3 ? ATTN_E_WORKSPACE : ATTN_E_ALIAS;
     }
+    attn::SeqLayout L{0, B, H, N, nullptr, nullptr, N, N, -1, causal ? 0 : -1};
+    attn::BwdParams p{q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, L, N, N, d, dtype, scale, stream};
+    return attn::launch_bwd(p) == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+namespace {
+
+// Checks shared by the packed variable-length entry points.
+int check_varlen(const int* cu_q, const int* cu_k, int batch, int H, int total_q, int total_k,
+                 int max_q, int max_k, int d, int causal, int wl, int wr, float scale, int dtype) {
+    if (batch < 0 || H < 0 || total_q < 0 || total_k < 0 || max_q < 0 || max_k < 0) return ATTN_E_SHAPE;
+    if (d != 64 && d != 128) return ATTN_E_UNSUPPORTED;
+    if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_E_UNSUPPORTED;
+    if (causal != 0 && causal != 1) return ATTN_E_UNSUPPORTED;
+    if (wl < -1 || wr < -1) return ATTN_E_UNSUPPORTED;
+    if (!isfinite(scale) || scale < 0.f) return ATTN_E_UNSUPPORTED;
+    if (batch == INT32_MAX) return ATTN_E_SHAPE;  // batch + 1 offsets must be addressable
+    if (batch > 0 && (!cu_q || !cu_k)) return ATTN_E_NULL;
+    if (!aligned(cu_q, 4) || !aligned(cu_k, 4)) return ATTN_E_ALIGN;
+    return ATTN_OK;
+}
+
+attn::SeqLayout varlen_layout(const int* cu_q, const int* cu_k, int batch, int H, int total_q, int total_k,
+                              int causal, int wl, int wr) {
+    return attn::SeqLayout{1, batch, H, 0, cu_q, cu_k, total_q, total_k, wl, causal ? 0 : wr};
+}
+
+}  // namespace
+
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* cu_seqlens_q,
+                    const int* cu_seqlens_k, int batch, int H, int total_q, int total_k, int max_seqlen_q,
+                    int d, int causal, int window_left, int window_right, float scale, int dtype, void* stream) {
+    int st = check_varlen(cu_seqlens_q, cu_seqlens_k, batch, H, total_q, total_k, max_seqlen_q, 0, d, causal,
+                          window_left, window_right, scale, dtype);
+    if (st != ATTN_OK) return st;
+    if ((int64_t)batch * H == 0 || total_q == 0 || max_seqlen_q == 0) return ATTN_OK;
+    if (!q || !o || !lse || (total_k > 0 && (!k || !v))) return ATTN_E_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+        return ATTN_E_ALIGN;
+    const size_t qb = (size_t)H * total_q * d * 2, kb = (size_t)H * total_k * d * 2, lb = (size_t)H * total_q * 4;
+    const Range rq = range_of(q, qb), rk = range_of(k, kb), rv = range_of(v, kb);
+    const Range ro = range_of(o, qb), rl = range_of(lse, lb);
+    const Range rcq = range_of(cu_seqlens_q, (size_t)(batch + 1) * 4), rck = range_of(cu_seqlens_k, (size_t)(batch + 1) * 4);
+    for (const Range& out : {ro, rl})
+        for (const Range& in : {rq, rk, rv, rcq, rck})
+            if (overlap(out, in)) return ATTN_E_ALIAS;
+    if (overlap(ro, rl)) return ATTN_E_ALIAS;
+    attn::FwdParams p{q, k, v, o, lse,
+                      varlen_layout(cu_seqlens_q, cu_seqlens_k, batch, H, total_q, total_k, causal, window_left,
+                                    window_right),
+                      max_seqlen_q, d, dtype, scale, stream};
+    return attn::launch_fwd(p) == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+size_t attn_bwd_varlen_workspace_bytes(int H, int total_q) {
+    if (H < 0 || total_q < 0) return (size_t)-1;
+    if ((int64_t)H * total_q == 0) return 0;
+    return attn::bwd_workspace_bytes_rows((int64_t)H * total_q);
+}
+
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                    void* dq, void* dk, void* dv, const int* cu_seqlens_q, const int* cu_seqlens_k, int batch,
+                    int H, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d, int causal,
+                    int window_left, int window_right, float scale, int dtype, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    int st = check_varlen(cu_seqlens_q, cu_seqlens_k, batch, H, total_q, total_k, max_seqlen_q, max_seqlen_k, d,
+                          causal, window_left, window_right, scale, dtype);
+    if (st != ATTN_OK) return st;
+    if ((int64_t)batch * H == 0 || (total_q == 0 && total_k == 0)) return ATTN_OK;
+    const bool has_q = total_q > 0, has_k = total_k > 0;
+    if ((has_q && (!q || !o || !dout || !lse || !dq)) || (has_k && (!k || !v || !dk || !dv))) return ATTN_E_NULL;
+    const size_t ws_need = attn::bwd_workspace_bytes_rows((int64_t)H * total_q);
+    if (ws_need > 0 && !workspace) return ATTN_E_WORKSPACE;
+    const void* a16[] = {q, k, v, o, dout, dq, dk, dv, workspace};
+    for (const void* ptr : a16)
+        if (!aligned(ptr, 16)) return ATTN_E_ALIGN;
+    if (!aligned(lse, 4)) return ATTN_E_ALIGN;
+    if (workspace_bytes < ws_need) return ATTN_E_WORKSPACE;
+    const size_t qb = (size_t)H * total_q * d * 2, kb = (size_t)H * total_k * d * 2, lb = (size_t)H * total_q * 4;
+    const Range ins[] = {range_of(q, qb), range_of(k, kb), range_of(v, kb), range_of(o, qb), range_of(dout, qb),
+                         range_of(lse, lb), range_of(cu_seqlens_q, (size_t)(batch + 1) * 4),
+                         range_of(cu_seqlens_k, (size_t)(batch + 1) * 4)};
+    const Range outs[] = {range_of(dq, qb), range_of(dk, kb), range_of(dv, kb), range_of(workspace, ws_need)};
+    for (int i = 0; i < 4; ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r)) return i == 3 ? ATTN_E_WORKSPACE : ATTN_E_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j])) return j == 3 ? ATTN_E_WORKSPACE : ATTN_E_ALIAS;
+    }
     attn::BwdParams p{q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace,
-                      B, H, N, d, causal, dtype, scale, stream};
+                      varlen_layout(cu_seqlens_q, cu_seqlens_k, batch, H, total_q, total_k, causal, window_left,
+                                    window_right),
+                      max_seqlen_q, max_seqlen_k, d, dtype, scale, stream};
     return attn::launch_bwd(p) == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 

@@ -95,13 +95,13 @@ __device__ inline void store_staged(uint16_t* __restrict__ dst, const uint16_t* 
 constexpr int kQ_BQ = 128;
 constexpr int kQ_BK = 64;
 
-template <class T, int D, bool CAUSAL>
+template <class T, int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                         const uint16_t* __restrict__ V, const uint16_t* __restrict__ O,
                         const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
-                        float* __restrict__ Delta, uint16_t* __restrict__ dQ, int N, int ntq, float scale,
-                        float c) {
+                        float* __restrict__ Delta, uint16_t* __restrict__ dQ, SeqLayout L, int ntq,
+                        float scale, float c) {
     constexpr int STR = LdsStride<D>::value;
     constexpr int KS = D / 16, DB = D / 32, KB = kQ_BK / 32;
     constexpr int TILE = kQ_BK * STR;
@@ -113,21 +113,23 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int n32 = lane & 31, h = lane >> 5;
     const int item = xcd_contiguous(blockIdx.x, gridDim.x);
-    const int bh = item / ntq;
-    const int qt = CAUSAL ? ntq - 1 - item % ntq : item % ntq;
-    const int64_t base = (int64_t)bh * N * D;
-    const uint16_t *Qh = Q + base, *Kh = K + base, *Vh = V + base, *Oh = O + base, *dOh = dO + base;
+    const Seq sq = resolve(L, item / ntq);
+    const int qt = (L.wr >= 0 && L.wl < 0) ? ntq - 1 - item % ntq : item % ntq;
     const int q0 = qt * kQ_BQ;
+    if (q0 >= sq.nq) return;  // the whole group: no barrier has been reached
+    const int nq = sq.nq, nk = sq.nk;
+    const uint16_t *Qh = Q + sq.qrow0 * D, *Oh = O + sq.qrow0 * D, *dOh = dO + sq.qrow0 * D;
+    const uint16_t *Kh = K + sq.krow0 * D, *Vh = V + sq.krow0 * D;
     const int wq0 = q0 + 32 * w;
     const int qrow = wq0 + n32;
-    const bool valid = qrow < N;
+    const bool valid = qrow < nq;
 
     // Resident Q^T and dO^T fragments; D = <dO, O> for this row.  Rows past
-    // the end read row N-1: their D is not stored, their lse is +inf (P = 0),
+    // the end read row nq-1: their D is not stored, their lse is +inf (P = 0),
     // and their dQ is not written.
     u32x4 qf[KS], dof[KS];
     float dpart = 0.f;
-    const int qrd = min(qrow, N - 1);
+    const int qrd = min(qrow, nq - 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         const int64_t off = (int64_t)qrd * D + 16 * ks + 8 * h;
@@ -137,18 +139,21 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
         dpart += dot8<T>(dof[ks], of);
     }
     const float Dq = sum_with_other_half(dpart);
-    if (h == 0 && valid) Delta[(int64_t)bh * N + qrow] = Dq;
-    const float lse2 = valid ? LSE[(int64_t)bh * N + qrd] * kLog2e : kPosInf;
+    if (h == 0 && valid) Delta[sq.qrow0 + qrow] = Dq;
+    const float lse2 = valid ? LSE[sq.qrow0 + qrd] * kLog2e : kPosInf;
 
-    const int kend = CAUSAL ? min(N, q0 + kQ_BQ) : N;
-    const int nkt = (kend + kQ_BK - 1) / kQ_BK;
-    // Leading key tiles visible in full to every row of the group.
-    const int nfull = min(N / kQ_BK, CAUSAL ? (q0 + 1) / kQ_BK : N / kQ_BK);
+    // Key tiles some row of the group sees, and those every row sees in full.
+    const int qlast = min(q0 + kQ_BQ, nq) - 1;
+    const TileRange tr = tile_range(sq.key_lo(q0), sq.key_hi(qlast), sq.key_lo(qlast),
+                                    min(sq.key_hi(q0), nk - 1), nk, kQ_BK);
     Copy kc(tid), vc(tid);
-    kc.load(Kh, 0, N, tid);
-    vc.load(Vh, 0, N, tid);
-    kc.store(Ks);
-    vc.store(Vs);
+    if (tr.end > tr.first) {
+        const int b0 = (tr.first & 1) * TILE;
+        kc.load(Kh, tr.first * kQ_BK, nk, tid);
+        vc.load(Vh, tr.first * kQ_BK, nk, tid);
+        kc.store(Ks + b0);
+        vc.store(Vs + b0);
+    }
     __syncthreads();
 
     f32x16 dqacc[DB];
@@ -162,12 +167,12 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
         constexpr bool MASKED = decltype(masked_tag)::value;
         const int buf = (jt & 1) * TILE;
         const int k0 = jt * kQ_BK;
-        const bool more = jt + 1 < nkt;
+        const bool more = jt + 1 < tr.end;
         if (more) {
-            kc.load(Kh, k0 + kQ_BK, N, tid);
-            vc.load(Vh, k0 + kQ_BK, N, tid);
+            kc.load(Kh, k0 + kQ_BK, nk, tid);
+            vc.load(Vh, k0 + kQ_BK, nk, tid);
         }
-        if (!(MASKED && CAUSAL) || k0 <= wq0 + 31) {
+        if (!MASKED || (wq0 < nq && k0 <= sq.key_hi(wq0 + 31) && k0 + kQ_BK - 1 >= sq.key_lo(wq0))) {
             // ---- S^T = K Q^T and dP^T = V dO^T
             f32x16 s[KB], dp[KB];
             prio_mfma();
@@ -188,6 +193,7 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
             sched_reads_ahead<4, 2 * KB * KS, 1>();
             prio_normal();
             // ---- P^T = exp(scale s - lse), dS^T = P^T o (dP^T - D)
+            const int klo = sq.key_lo(qrow), khi = min(sq.key_hi(qrow), nk - 1);
             u32x4 b[KB][2];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
@@ -197,7 +203,7 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                     float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e], c, -lse2));
                     if constexpr (MASKED) {
                         const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-                        if (key >= N || (CAUSAL && key > qrow)) p = 0.f;
+                        if (key < klo || key > khi) p = 0.f;
                     }
                     ds[e] = p * (dp[kb][e] - Dq);
                 }
@@ -222,12 +228,13 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
         }
         __syncthreads();
     };
-    for (int jt = 0; jt < nfull; ++jt) step(jt, Flag<false>{});
-    for (int jt = nfull; jt < nkt; ++jt) step(jt, Flag<true>{});
+    for (int jt = tr.first; jt < tr.full_first; ++jt) step(jt, Flag<true>{});
+    for (int jt = tr.full_first; jt < tr.full_end; ++jt) step(jt, Flag<false>{});
+    for (int jt = tr.full_end; jt < tr.end; ++jt) step(jt, Flag<true>{});
 
     stage_transposed<T, D, STR>(Ks, 32 * w + n32, h, dqacc, scale);
     __syncthreads();
-    store_staged<D, STR>(dQ + base, Ks, kQ_BQ, q0, N, tid);
+    store_staged<D, STR>(dQ + sq.qrow0 * D, Ks, kQ_BQ, q0, nq, tid);
 }
 
 // ============================================================================
@@ -239,13 +246,13 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 constexpr int kK_BK = 128;
 constexpr int kK_BQ = 64;
 
-template <class T, int D, bool CAUSAL>
+template <class T, int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(D == 64 ? 2 : 1, 2)))
 void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                           const float* __restrict__ LSE, const float* __restrict__ Delta,
-                          uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int ntk, float scale,
-                          float c) {
+                          uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, SeqLayout L, int ntk,
+                          float scale, float c) {
     constexpr int STR = LdsStride<D>::value;
     constexpr int KS = D / 16, DB = D / 32, QB = kK_BQ / 32;
     constexpr int TILE = kK_BQ * STR;
@@ -258,20 +265,22 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int n32 = lane & 31, h = lane >> 5;
     const int item = xcd_contiguous(blockIdx.x, gridDim.x);
-    const int bh = item / ntk;
+    const Seq sq = resolve(L, item / ntk);
     const int kt = item % ntk;  // causal: low key tiles see the most queries and run first
-    const int64_t base = (int64_t)bh * N * D;
-    const uint16_t *Qh = Q + base, *Kh = K + base, *Vh = V + base, *dOh = dO + base;
-    const float* lseh = LSE + (int64_t)bh * N;
-    const float* Dh = Delta + (int64_t)bh * N;
     const int k0 = kt * kK_BK;
+    if (k0 >= sq.nk) return;  // the whole group: no barrier has been reached
+    const int nq = sq.nq, nk = sq.nk;
+    const uint16_t *Qh = Q + sq.qrow0 * D, *dOh = dO + sq.qrow0 * D;
+    const uint16_t *Kh = K + sq.krow0 * D, *Vh = V + sq.krow0 * D;
+    const float* lseh = LSE + sq.qrow0;
+    const float* Dh = Delta + sq.qrow0;
     const int wk0 = k0 + 32 * w;
     const int krow = wk0 + n32;
 
     // Resident K and V fragments (B operands of S = Q K^T and dP = dO V^T).
-    // Keys past the end read row N-1; their dK and dV are never written.
+    // Keys past the end read row nk-1; their dK and dV are never written.
     u32x4 kf[KS], vf[KS];
-    const int krd = min(krow, N - 1);
+    const int krd = min(krow, nk - 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         const int64_t off = (int64_t)krd * D + 16 * ks + 8 * h;
@@ -279,18 +288,18 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         vf[ks] = *(const u32x4*)(Vh + off);
     }
 
-    const int q_start = CAUSAL ? (k0 / kK_BQ) * kK_BQ : 0;
-    const int nqt = (N - q_start + kK_BQ - 1) / kK_BQ;
-    // Query tiles that straddle the keys of the group need the causal mask;
-    // rows past the end need none (their lse is +inf, so P = 0).
-    const int nmask = CAUSAL ? min(nqt, (k0 + kK_BK - q_start + kK_BQ - 1) / kK_BQ) : 0;
+    // Query tiles in which some row sees a key of the group, and those whose
+    // every row sees every key of the group (rows past the end need no mask:
+    // their lse is +inf, so P = 0).
+    const int klast = min(k0 + kK_BK, nk) - 1;
+    const TileRange tr = tile_range(sq.row_lo(k0), sq.row_hi(klast), sq.row_lo(klast), sq.row_hi(k0), nq, kK_BQ);
     Copy qc(tid), oc(tid);
     float st_l = kPosInf, st_d = 0.f;
     auto load_stats = [&](int r0) {
         if (tid < kK_BQ) {
             const int r = r0 + tid;
-            st_l = r < N ? lseh[r] * kLog2e : kPosInf;  // rows past the end get P = 0
-            st_d = r < N ? Dh[r] : 0.f;
+            st_l = r < nq ? lseh[r] * kLog2e : kPosInf;  // rows past the end get P = 0
+            st_d = r < nq ? Dh[r] : 0.f;
         }
     };
     auto store_stats = [&](int sb) {
@@ -299,12 +308,15 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
             stats[sb][1][tid] = st_d;
         }
     };
-    qc.load(Qh, q_start, N, tid);
-    oc.load(dOh, q_start, N, tid);
-    load_stats(q_start);
-    qc.store(Qs);
-    oc.store(dOs);
-    store_stats(0);
+    if (tr.end > tr.first) {
+        const int r0 = tr.first * kK_BQ, sb0 = tr.first & 1;
+        qc.load(Qh, r0, nq, tid);
+        oc.load(dOh, r0, nq, tid);
+        load_stats(r0);
+        qc.store(Qs + sb0 * TILE);
+        oc.store(dOs + sb0 * TILE);
+        store_stats(sb0);
+    }
     __syncthreads();
 
     f32x16 dkacc[DB], dvacc[DB];
@@ -321,17 +333,18 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         constexpr bool MASKED = decltype(masked_tag)::value;
         const int sb = it & 1;
         const int buf = sb * TILE;
-        const int qq0 = q_start + it * kK_BQ;
-        const bool more = it + 1 < nqt;
+        const int qq0 = it * kK_BQ;
+        const bool more = it + 1 < tr.end;
         if (more) {
-            qc.load(Qh, qq0 + kK_BQ, N, tid);
-            oc.load(dOh, qq0 + kK_BQ, N, tid);
+            qc.load(Qh, qq0 + kK_BQ, nq, tid);
+            oc.load(dOh, qq0 + kK_BQ, nq, tid);
             load_stats(qq0 + kK_BQ);
         }
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const int qb0 = qq0 + 32 * qb;  // first query row of this 32-row block
-            if (MASKED && qb0 + 31 < wk0) continue;  // every query precedes every key of this wave
+            // skip a block none of whose rows sees a key of this wave
+            if (MASKED && (qb0 + 31 < sq.row_lo(wk0) || qb0 > sq.row_hi(wk0 + 31))) continue;
             // ---- S = Q K^T and dP = dO V^T
             f32x16 s, dp;
 #pragma unroll
@@ -366,7 +379,7 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
             for (int e = 0; e < 16; ++e) {
                 float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -ls[e]));
                 if constexpr (MASKED) {
-                    if (qb0 + 8 * (e >> 2) + 4 * h + (e & 3) < krow) pe = 0.f;
+                    if (!sq.visible(qb0 + 8 * (e >> 2) + 4 * h + (e & 3), krow)) pe = 0.f;
                 }
                 p[e] = pe;
                 ds[e] = pe * (dp[e] - dd[e]);
@@ -393,45 +406,45 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         }
         __syncthreads();
     };
-    for (int it = 0; it < nmask; ++it) step(it, Flag<true>{});
-    for (int it = nmask; it < nqt; ++it) step(it, Flag<false>{});
+    for (int it = tr.first; it < tr.full_first; ++it) step(it, Flag<true>{});
+    for (int it = tr.full_first; it < tr.full_end; ++it) step(it, Flag<false>{});
+    for (int it = tr.full_end; it < tr.end; ++it) step(it, Flag<true>{});
 
     stage_transposed<T, D, STR>(Qs, 32 * w + n32, h, dkacc, scale);
     __syncthreads();
-    store_staged<D, STR>(dK + base, Qs, kK_BK, k0, N, tid);
+    store_staged<D, STR>(dK + sq.krow0 * D, Qs, kK_BK, k0, nk, tid);
     __syncthreads();
     stage_transposed<T, D, STR>(Qs, 32 * w + n32, h, dvacc, 1.f);
     __syncthreads();
-    store_staged<D, STR>(dV + base, Qs, kK_BK, k0, N, tid);
-}
-
-template <class T, int D, bool CAUSAL>
-hipError_t launch(const BwdParams& p) {
-    const int ntq = (p.N + kQ_BQ - 1) / kQ_BQ;
-    const int ntk = (p.N + kK_BK - 1) / kK_BK;
-    const int64_t bh = (int64_t)p.B * p.H;
-    if (bh * ntq > 0x7fffffff || bh * ntk > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const float c = p.scale * kLog2e;
-    hipStream_t st = (hipStream_t)p.stream;
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)(bh * ntq)), dim3(kThreads), 0, st,
-                       (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v, (const uint16_t*)p.o,
-                       (const uint16_t*)p.dout, p.lse, p.delta, (uint16_t*)p.dq, p.N, ntq, p.scale, c);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, CAUSAL>), dim3((unsigned)(bh * ntk)), dim3(kThreads), 0, st,
-                       (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v, (const uint16_t*)p.dout,
-                       p.lse, p.delta, (uint16_t*)p.dk, (uint16_t*)p.dv, p.N, ntk, p.scale, c);
-    return hipGetLastError();
+    store_staged<D, STR>(dV + sq.krow0 * D, Qs, kK_BK, k0, nk, tid);
 }
 
 template <class T, int D>
-hipError_t launch_c(const BwdParams& p) {
-    return p.causal ? launch<T, D, true>(p) : launch<T, D, false>(p);
+hipError_t launch(const BwdParams& p) {
+    const int ntq = (p.max_nq + kQ_BQ - 1) / kQ_BQ;
+    const int ntk = (p.max_nk + kK_BK - 1) / kK_BK;
+    const int64_t nseq = (int64_t)p.L.B * p.L.H;
+    if (nseq * ntq > 0x7fffffff || nseq * ntk > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const float c = p.scale * kLog2e;
+    hipStream_t st = (hipStream_t)p.stream;
+    if (nseq * ntq > 0) {
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D>), dim3((unsigned)(nseq * ntq)), dim3(kThreads), 0, st,
+                           (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v, (const uint16_t*)p.o,
+                           (const uint16_t*)p.dout, p.lse, p.delta, (uint16_t*)p.dq, p.L, ntq, p.scale, c);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (nseq * ntk > 0) {
+        hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D>), dim3((unsigned)(nseq * ntk)), dim3(kThreads), 0, st,
+                           (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v, (const uint16_t*)p.dout,
+                           p.lse, p.delta, (uint16_t*)p.dk, (uint16_t*)p.dv, p.L, ntk, p.scale, c);
+    }
+    return hipGetLastError();
 }
 
 template <class T>
 hipError_t launch_d(const BwdParams& p) {
-    return p.d == 64 ? launch_c<T, 64>(p) : launch_c<T, 128>(p);
+    return p.d == 64 ? launch<T, 64>(p) : launch<T, 128>(p);
 }
 
 }  // namespace

@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attn_launch.h"
+
 namespace attn {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -232,6 +234,72 @@ __device__ inline void sched_reads_ahead() {
 // the other wave on the SIMD fills the gaps with VALU work.
 __device__ inline void prio_mfma() { __builtin_amdgcn_s_setprio(1); }
 __device__ inline void prio_normal() { __builtin_amdgcn_s_setprio(0); }
+
+// One sequence of a call, resolved on the device (see SeqLayout).
+struct Seq {
+    int64_t qrow0, krow0;  // global row index of query row 0 / key row 0
+    int nq, nk;
+    int off;     // query row i sits at key position i + off
+    int wl, wr;  // window bounds (-1: unbounded)
+
+    // First and last key (inclusive, before clipping to [0, nk)) visible to row i.
+    __device__ inline int key_lo(int i) const { return wl < 0 ? -0x3fffffff : i + off - wl; }
+    __device__ inline int key_hi(int i) const { return wr < 0 ? 0x3fffffff : i + off + wr; }
+    // First and last query row (inclusive, before clipping) that sees key j.
+    __device__ inline int row_lo(int j) const { return wr < 0 ? -0x3fffffff : j - off - wr; }
+    __device__ inline int row_hi(int j) const { return wl < 0 ? 0x3fffffff : j - off + wl; }
+    __device__ inline bool visible(int i, int j) const {
+        return j >= key_lo(i) && j <= key_hi(i);
+    }
+};
+
+__device__ inline Seq resolve(const SeqLayout& L, int s) {
+    Seq r;
+    r.wl = L.wl;
+    r.wr = L.wr;
+    if (L.mode == 0) {
+        r.qrow0 = r.krow0 = (int64_t)s * L.N;
+        r.nq = r.nk = L.N;
+        r.off = 0;
+        return r;
+    }
+    const int h = s / L.B, b = s % L.B;
+    const int q0 = min(max(L.cu_q[b], 0), L.total_q), q1 = min(max(L.cu_q[b + 1], q0), L.total_q);
+    const int k0 = min(max(L.cu_k[b], 0), L.total_k), k1 = min(max(L.cu_k[b + 1], k0), L.total_k);
+    r.qrow0 = (int64_t)h * L.total_q + q0;
+    r.krow0 = (int64_t)h * L.total_k + k0;
+    r.nq = q1 - q0;
+    r.nk = k1 - k0;
+    r.off = r.nk - r.nq;
+    return r;
+}
+
+// Tiles [first, end) of size BT that hold an index in [lo, hi] (inclusive,
+// clipped to [0, n); empty when nothing is left), and the sub-range
+// [full_first, full_end) of those tiles whose every index lies in
+// [all_lo, all_hi] (the caller clips all_hi as the use requires).
+struct TileRange {
+    int first, end, full_first, full_end;
+};
+
+__device__ inline TileRange tile_range(int lo, int hi, int all_lo, int all_hi, int n, int bt) {
+    TileRange t;
+    lo = max(lo, 0);
+    hi = min(hi, n - 1);
+    if (hi < lo) {
+        t.first = t.end = t.full_first = t.full_end = 0;
+        return t;
+    }
+    t.first = lo / bt;
+    t.end = hi / bt + 1;
+    all_lo = max(all_lo, 0);
+    int ff = (all_lo + bt - 1) / bt, fe = all_hi < all_lo ? ff : (all_hi + 1) / bt;
+    ff = min(max(ff, t.first), t.end);
+    fe = min(max(fe, ff), t.end);
+    t.full_first = ff;
+    t.full_end = fe;
+    return t;
+}
 
 // Work groups are handed to the 8 XCDs round-robin (block b runs on XCD b % 8).
 // Renumber them so that each XCD receives one contiguous range of work items:

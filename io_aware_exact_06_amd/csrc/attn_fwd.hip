@@ -60,12 +60,12 @@ struct FwdShape {
     static_assert(BQ * STR <= 4 * TILE, "output staging must fit in the tile buffers");
 };
 
-template <class T, int D, bool CAUSAL, int QB>
+template <class T, int D, int QB>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(QB == 1 ? 2 : 1, QB == 1 ? 2 : 1)))
 void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                     float* __restrict__ LSE, int N, int ntq, float scale, float c) {
+                     float* __restrict__ LSE, SeqLayout L, int ntq, float scale, float c) {
     using S = FwdShape<D, QB>;
     __shared__ __attribute__((aligned(16))) uint16_t smem[4 * S::TILE];
     uint16_t* const Ks = smem;               // two K tiles
@@ -74,38 +74,44 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int n32 = lane & 31, h = lane >> 5;
 
-    // Work item: (batch*head, query tile).  Each XCD gets a contiguous range;
-    // within a head, causal tiles run longest first.
+    // Work item: (sequence, query tile).  Each XCD gets a contiguous range;
+    // when rows see only keys up to a right bound (causal), tiles run longest
+    // first.
     const int item = xcd_contiguous(blockIdx.x, gridDim.x);
-    const int bh = item / ntq;
-    const int qt = CAUSAL ? ntq - 1 - item % ntq : item % ntq;
-    const int64_t base = (int64_t)bh * N * D;
-    const uint16_t* Qh = Q + base;
-    const uint16_t* Kh = K + base;
-    const uint16_t* Vh = V + base;
+    const Seq sq = resolve(L, item / ntq);
+    const int qt = (L.wr >= 0 && L.wl < 0) ? ntq - 1 - item % ntq : item % ntq;
     const int q0 = qt * S::BQ;
+    if (q0 >= sq.nq) return;  // the whole group: no barrier has been reached
+    const int nq = sq.nq, nk = sq.nk;
+    const uint16_t* Qh = Q + sq.qrow0 * D;
+    const uint16_t* Kh = K + sq.krow0 * D;
+    const uint16_t* Vh = V + sq.krow0 * D;
     const int wq0 = q0 + w * 32 * QB;  // first row of this wave; block qb starts at wq0 + 32 qb
 
     // Q^T fragments (B operand of S^T = K Q^T), resident for the whole loop.
-    // Rows past the end read row N-1; their outputs are never stored.
+    // Rows past the end read row nq-1; their outputs are never stored.
     u32x4 qf[QB][S::KS];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        const int qrow = min(wq0 + 32 * qb + n32, N - 1);
+        const int qrow = min(wq0 + 32 * qb + n32, nq - 1);
 #pragma unroll
         for (int ks = 0; ks < S::KS; ++ks) qf[qb][ks] = *(const u32x4*)(Qh + (int64_t)qrow * D + 16 * ks + 8 * h);
     }
 
-    const int kend = CAUSAL ? min(N, q0 + S::BQ) : N;
-    const int nkt = (kend + kBK - 1) / kBK;
-    // Leading tiles whose keys are all visible to every row of the group.
-    const int nfull = min(N / kBK, CAUSAL ? (q0 + 1) / kBK : N / kBK);
+    // Key tiles some row of the group sees, and those every row sees in full
+    // (which run without any per-element test).
+    const int qlast = min(q0 + S::BQ, nq) - 1;
+    const TileRange tr = tile_range(sq.key_lo(q0), sq.key_hi(qlast), sq.key_lo(qlast),
+                                    min(sq.key_hi(q0), nk - 1), nk, kBK);
 
     TileCopy<kBK, D, kThreads> kc(tid), vc(tid);
-    kc.load(Kh, 0, N, tid);
-    vc.load(Vh, 0, N, tid);
-    kc.store(Ks);
-    vc.store(Vs);
+    if (tr.end > tr.first) {
+        const int b0 = (tr.first & 1) * S::TILE;
+        kc.load(Kh, tr.first * kBK, nk, tid);
+        vc.load(Vh, tr.first * kBK, nk, tid);
+        kc.store(Ks + b0);
+        vc.store(Vs + b0);
+    }
     __syncthreads();
 
     f32x16 oacc[QB][S::DB];
@@ -131,16 +137,21 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         constexpr bool MASKED = decltype(masked_tag)::value;
         const int buf = (jt & 1) * S::TILE;
         const int k0 = jt * kBK;
-        const bool more = jt + 1 < nkt;
+        const bool more = jt + 1 < tr.end;
         if (more) {
-            kc.load(Kh, k0 + kBK, N, tid);
-            vc.load(Vh, k0 + kBK, N, tid);
+            kc.load(Kh, k0 + kBK, nk, tid);
+            vc.load(Vh, k0 + kBK, nk, tid);
         }
         // Query blocks of this wave that see at least one key of the tile.
         bool act[QB];
+        bool any = false;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) act[qb] = !(MASKED && CAUSAL) || k0 <= wq0 + 32 * qb + 31;
-        if (act[QB - 1]) {
+        for (int qb = 0; qb < QB; ++qb) {
+            const int r0 = wq0 + 32 * qb;
+            act[qb] = !MASKED || (r0 < nq && k0 <= sq.key_hi(r0 + 31) && k0 + kBK - 1 >= sq.key_lo(r0));
+            any = any || act[qb];
+        }
+        if (any) {
             // ---- S^T = K Q^T: each K fragment feeds every active query block
             f32x16 s[QB][S::KB];
 #pragma unroll
@@ -168,14 +179,15 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             for (int qb = 0; qb < QB; ++qb) {
                 if (!act[qb]) continue;
                 if constexpr (MASKED) {
-                    // ---- mask keys past the end and (causal) keys after the row
+                    // ---- mask keys past the end and keys outside the row's window
                     const int qrow = wq0 + 32 * qb + n32;
+                    const int klo = sq.key_lo(qrow), khi = min(sq.key_hi(qrow), nk - 1);
 #pragma unroll
                     for (int kb = 0; kb < S::KB; ++kb)
 #pragma unroll
                         for (int e = 0; e < 16; ++e) {
                             const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-                            if (key >= N || (CAUSAL && key > qrow)) s[qb][kb][e] = kNegInf;
+                            if (key < klo || key > khi) s[qb][kb][e] = kNegInf;
                         }
                 }
                 // ---- online softmax: raise the maximum, rescale when it grew
@@ -233,8 +245,9 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         }
         __syncthreads();
     };
-    for (int jt = 0; jt < nfull; ++jt) step(jt, Flag<false>{});
-    for (int jt = nfull; jt < nkt; ++jt) step(jt, Flag<true>{});
+    for (int jt = tr.first; jt < tr.full_first; ++jt) step(jt, Flag<true>{});
+    for (int jt = tr.full_first; jt < tr.full_end; ++jt) step(jt, Flag<false>{});
+    for (int jt = tr.full_end; jt < tr.end; ++jt) step(jt, Flag<true>{});
 
     // ---- epilogue: O = O^T / l, staged through LDS for row-contiguous stores
     uint16_t* Os = smem;  // the loop ended on a barrier: every tile buffer is free
@@ -242,8 +255,9 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     for (int qb = 0; qb < QB; ++qb) {
         const int qrow = wq0 + 32 * qb + n32;
         const float lt = sum_with_other_half(l[qb]);
-        const float inv = 1.f / lt;
-        if (h == 0 && qrow < N) LSE[(int64_t)bh * N + qrow] = m[qb] * scale + logf(lt);
+        // a row that sees no key at all: O = 0, lse = -inf
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        if (h == 0 && qrow < nq) LSE[sq.qrow0 + qrow] = lt > 0.f ? m[qb] * scale + logf(lt) : kNegInf;
         const int orow = (w * 32 * QB + 32 * qb + n32) * S::STR;
 #pragma unroll
         for (int db = 0; db < S::DB; ++db)
@@ -255,39 +269,31 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             }
     }
     __syncthreads();
-    uint16_t* Oh = O + base;
+    uint16_t* Oh = O + sq.qrow0 * D;
     for (int ch = tid; ch < S::BQ * S::CH; ch += kThreads) {
         const int r = ch / S::CH, col = ch % S::CH;
-        if (q0 + r < N) *(u32x4*)(Oh + (int64_t)(q0 + r) * D + 8 * col) = *(const u32x4*)(Os + r * S::STR + 8 * col);
+        if (q0 + r < nq) *(u32x4*)(Oh + (int64_t)(q0 + r) * D + 8 * col) = *(const u32x4*)(Os + r * S::STR + 8 * col);
     }
 }
 
-template <class T, int D, bool CAUSAL, int QB>
+template <class T, int D, int QB>
 hipError_t launch_qb(const FwdParams& p) {
     using S = FwdShape<D, QB>;
-    const int ntq = (p.N + S::BQ - 1) / S::BQ;
-    const int64_t blocks = (int64_t)p.B * p.H * ntq;
+    const int ntq = (p.max_nq + S::BQ - 1) / S::BQ;
+    const int64_t nseq = (int64_t)p.L.B * p.L.H;
+    const int64_t blocks = nseq * ntq;
+    if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D, CAUSAL, QB>), dim3((unsigned)blocks), dim3(kThreads), 0,
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, QB>), dim3((unsigned)blocks), dim3(kThreads), 0,
                        (hipStream_t)p.stream, (const uint16_t*)p.q, (const uint16_t*)p.k,
-                       (const uint16_t*)p.v, (uint16_t*)p.o, p.lse, p.N, ntq, p.scale,
+                       (const uint16_t*)p.v, (uint16_t*)p.o, p.lse, p.L, ntq, p.scale,
                        p.scale * kLog2e);
     return hipGetLastError();
 }
 
-template <class T, int D, bool CAUSAL>
-hipError_t launch(const FwdParams& p) {
-    return launch_qb<T, D, CAUSAL, ATTN_FWD_QB>(p);
-}
-
-template <class T, int D>
-hipError_t launch_c(const FwdParams& p) {
-    return p.causal ? launch<T, D, true>(p) : launch<T, D, false>(p);
-}
-
 template <class T>
 hipError_t launch_d(const FwdParams& p) {
-    return p.d == 64 ? launch_c<T, 64>(p) : launch_c<T, 128>(p);
+    return p.d == 64 ? launch_qb<T, 64, ATTN_FWD_QB>(p) : launch_qb<T, 128, ATTN_FWD_QB>(p);
 }
 
 }  // namespace

@@ -11,13 +11,37 @@ namespace attn {
 constexpr int kDtypeF16 = 0;
 constexpr int kDtypeBF16 = 1;
 
+// Where the sequences of a call live and which keys each query row sees.
+//
+// Dense calls (mode 0): tensors [B, H, N, d]; sequence s = b*H + h owns rows
+// s*N .. s*N+N-1 of both the query and the key arrays.
+// Packed calls (mode 1): tensors [H, total, d]; sequence s = h*B + b (B is the
+// number of sequences) owns query rows cu_q[b] .. cu_q[b+1]-1 and key rows
+// cu_k[b] .. cu_k[b+1]-1 of head h (cu_* are device int32 arrays, clamped to
+// [0, total] and made non-decreasing on the device before use).
+//
+// Query row i of a sequence with nq rows and nk keys sits at key position
+// pos = i + nk - nq (rows aligned to the end of the keys).  Key j is visible
+// iff (wl < 0 or j >= pos - wl) and (wr < 0 or j <= pos + wr); a causal call
+// is wr = 0.
+struct SeqLayout {
+    int mode;
+    int B, H, N;
+    const int* cu_q;
+    const int* cu_k;
+    int total_q, total_k;
+    int wl, wr;
+};
+
 struct FwdParams {
     const void* q;
     const void* k;
     const void* v;
     void* o;
     float* lse;
-    int B, H, N, d, causal, dtype;
+    SeqLayout L;
+    int max_nq;  // longest query sequence (grid size)
+    int d, dtype;
     float scale;
     void* stream;
 };
@@ -32,15 +56,18 @@ struct BwdParams {
     void* dq;
     void* dk;
     void* dv;
-    float* delta;  // fp32 [B, H, N] row terms D_i = <dO_i, O_i>: the caller's workspace
-    int B, H, N, d, causal, dtype;
+    float* delta;  // fp32 row terms D_i = <dO_i, O_i>, one per query row: the caller's workspace
+    SeqLayout L;
+    int max_nq, max_nk;  // longest query / key sequences (grid sizes)
+    int d, dtype;
     float scale;
     void* stream;
 };
 
-// Bytes of backward workspace: one fp32 D per query row, rounded up to 256.
-inline size_t bwd_workspace_bytes(int64_t B, int64_t H, int64_t N) {
-    return (((size_t)(B * H * N) * sizeof(float)) + 255) & ~(size_t)255;
+// Bytes of backward workspace for `rows` query rows: one fp32 D per row,
+// rounded up to a multiple of 256.
+inline size_t bwd_workspace_bytes_rows(int64_t rows) {
+    return (((size_t)rows * sizeof(float)) + 255) & ~(size_t)255;
 }
 
 hipError_t launch_fwd(const FwdParams& p);

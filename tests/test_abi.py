@@ -94,3 +94,52 @@ def test_bwd_rejects(kw, status):
 
 def test_bwd_empty_problem_is_a_no_op():
     assert bwd(q=0, k=0, v=0, o=0, dout=0, lse=0, dq=0, dk=0, dv=0, ws=0, ws_bytes=0, N=0) == 0
+
+
+def fwd_varlen(q=A, k=A + 0x100000, v=A + 0x200000, o=A + 0x300000, lse=A + 0x400000, cu_q=A + 0x500000,
+               cu_k=A + 0x500100, batch=2, H=2, tq=64, tk=80, max_q=40, d=64, causal=0, wl=-1, wr=-1,
+               scale=0.125, dtype=1):
+    return attn.attn_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, batch, H, tq, tk, max_q, d, causal, wl, wr, scale,
+                                dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu_q=0), 1), (dict(q=0), 1), (dict(k=0), 1), (dict(lse=0), 1),
+    (dict(batch=-1), 2), (dict(tq=-5), 2), (dict(max_q=-1), 2),
+    (dict(d=48), 3), (dict(wl=-2), 3), (dict(wr=-3), 3), (dict(causal=3), 3), (dict(scale=-0.5), 3),
+    (dict(cu_k=A + 0x500102), 4), (dict(o=A + 0x300008), 4),
+    (dict(o=A + 0x100010), 5), (dict(lse=A + 0x500000 - 8), 5), (dict(o=A + 0x500000 - 16), 5),
+])
+def test_fwd_varlen_rejects(kw, status):
+    assert fwd_varlen(**kw) == status
+
+
+def test_fwd_varlen_empty_calls_are_no_ops():
+    assert fwd_varlen(q=0, k=0, v=0, o=0, lse=0, tq=0) == 0
+    assert fwd_varlen(q=0, k=0, v=0, o=0, lse=0, max_q=0) == 0
+    assert fwd_varlen(q=0, k=0, v=0, o=0, lse=0, cu_q=0, cu_k=0, batch=0) == 0
+
+
+def test_bwd_varlen_workspace_and_rejects():
+    n = attn.attn_bwd_varlen_workspace_bytes(3, 1000)
+    assert n >= 3 * 1000 * 4 and n % 256 == 0
+    assert attn.attn_bwd_varlen_workspace_bytes(0, 1000) == 0
+    args = dict(q=A, k=A + 0x100000, v=A + 0x200000, o=A + 0x300000, dout=A + 0x400000, lse=A + 0x500000,
+                dq=A + 0x600000, dk=A + 0x700000, dv=A + 0x800000, cu_q=A + 0x900000, cu_k=A + 0x900100,
+                batch=2, H=2, tq=64, tk=80, max_q=40, max_k=50, d=64, causal=1, wl=-1, wr=-1, scale=0.1,
+                dtype=0, ws=A + 0xA00000, ws_bytes=attn.attn_bwd_varlen_workspace_bytes(2, 64))
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return attn.attn_bwd_varlen(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"],
+                                    a["dv"], a["cu_q"], a["cu_k"], a["batch"], a["H"], a["tq"], a["tk"],
+                                    a["max_q"], a["max_k"], a["d"], a["causal"], a["wl"], a["wr"], a["scale"],
+                                    a["dtype"], a["ws"], a["ws_bytes"], None)
+    assert call(dq=0) == 1
+    assert call(ws=0) == 6
+    assert call(ws_bytes=16) == 6
+    assert call(dk=A + 0x100000) == 5
+    assert call(ws=A + 0x900000) == 6
+    assert call(max_k=-1) == 2
+    assert call(q=0, k=0, v=0, o=0, dout=0, lse=0, dq=0, dk=0, dv=0, tq=0, tk=0) == 0

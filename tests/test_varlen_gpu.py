@@ -1,0 +1,111 @@
+"""Packed variable-length batches, rectangular (end-aligned) shapes and sliding
+windows on the GPU, through attn_fwd_varlen / attn_bwd_varlen, against the fp64
+oracle's per-sequence computation."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from io_aware_exact_06_amd import attn
+from io_aware_exact_06_amd.inputs import DTYPES, default_scale, make_inputs
+from tests.tolerance import GRAD_TOL, lse_report, o_report, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def packed_inputs(lq, lk, H, d, dtype, seed):
+    """Packed [H, total, d] tensors drawn with the seeded generator (B=1, N=total)."""
+    tq, tk = sum(lq), sum(lk)
+    a = make_inputs(1, H, max(tq, 1), d, dtype, seed, with_dout=True)
+    b = make_inputs(1, H, max(tk, 1), d, dtype, seed + 1)
+    q, do = a["q"][0, :, :tq].contiguous(), a["dout"][0, :, :tq].contiguous()
+    k, v = b["k"][0, :, :tk].contiguous(), b["v"][0, :, :tk].contiguous()
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    return q, k, v, do, cu_q, cu_k
+
+
+def check_lse(l_gpu, l_ref, label):
+    inf_ref = np.isneginf(l_ref)
+    assert np.array_equal(np.isneginf(l_gpu), inf_ref), label + ": rows without keys differ"
+    rep = lse_report(l_gpu[~inf_ref], l_ref[~inf_ref])
+    assert rep["ok"], (label, rep)
+    return rep
+
+
+CASES = [
+    # lq, lk, H, d, dtype, causal, window
+    ([1, 65, 130, 0, 257], [1, 65, 130, 0, 257], 2, 128, "bf16", True, (-1, -1)),
+    ([300, 17, 129], [300, 17, 129], 2, 64, "f16", False, (64, 31)),
+    ([50, 1, 200], [300, 40, 200], 2, 128, "f16", True, (-1, -1)),
+    ([100, 7], [40, 70], 1, 64, "bf16", True, (-1, -1)),
+    ([1000], [1000], 2, 128, "bf16", True, (255, -1)),
+    ([333, 90], [333, 500], 1, 128, "f16", False, (-1, -1)),
+    ([5, 3], [0, 4], 1, 64, "f16", False, (-1, -1)),
+    ([513], [513], 2, 64, "bf16", False, (100, 0)),
+]
+
+
+@pytest.mark.parametrize("lq,lk,H,d,dtype,causal,window", CASES)
+def test_varlen_fwd_bwd(lq, lk, H, d, dtype, causal, window):
+    label = "varlen lq=%s lk=%s H%d d%d %s causal=%d window=%s" % (lq, lk, H, d, dtype, causal, window)
+    say(label)
+    q, k, v, do, cu_q, cu_k = packed_inputs(lq, lk, H, d, dtype, seed=sum(lq) + 3 * sum(lk) + d)
+    scale = default_scale(d)
+    dev = torch.device("cuda")
+    gq, gk, gv, gdo = (t.to(dev) for t in (q, k, v, do))
+    tcq, tck = torch.from_numpy(cu_q).to(dev), torch.from_numpy(cu_k).to(dev)
+    o, lse = attn.fwd_varlen(gq, gk, gv, tcq, tck, max(lq), causal, scale, window)
+    dq, dk, dv = attn.bwd_varlen(gq, gk, gv, o, gdo, lse, tcq, tck, max(lq), max(lk), causal, scale, window)
+    torch.cuda.synchronize()
+    ro, rl = oracle.fwd_varlen(q.double().numpy(), k.double().numpy(), v.double().numpy(), cu_q, cu_k,
+                               causal, scale, window)
+    rep = o_report(o.float().cpu().numpy(), ro, dtype)
+    assert rep["ok"], (label, rep)
+    lrep = check_lse(lse.cpu().numpy(), rl, label)
+    rq, rk, rv = oracle.bwd_varlen(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                   do.double().numpy(), cu_q, cu_k, causal, scale, window)
+    errs = [rel_l2(a.float().cpu().numpy(), r) for a, r in ((dq, rq), (dk, rk), (dv, rv))]
+    say("  O max_abs %.3g, lse %.3g, grads %.3g %.3g %.3g" % (rep["max_abs"], lrep["max_floored_rel"], *errs))
+    assert max(errs) <= GRAD_TOL, errs
+    # rows that see no key have zero O and zero dQ, exactly
+    none = np.isneginf(rl)
+    assert np.all(o.float().cpu().numpy()[none] == 0) and np.all(dq.float().cpu().numpy()[none] == 0)
+
+
+def test_dense_equals_packed_single_sequence():
+    """The dense call [1, H, N, d] and the packed call with one sequence share
+    rows, so they must agree bitwise (forward and backward)."""
+    say("dense vs packed, one sequence")
+    H, N, d = 3, 777, 128
+    inp = make_inputs(1, H, N, d, "bf16", seed=21, with_dout=True)
+    q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "dout"))
+    cu = torch.tensor([0, N], dtype=torch.int32, device="cuda")
+    for causal in (False, True):
+        o1, l1 = attn.fwd(q, k, v, causal, 0.1)
+        o2, l2 = attn.fwd_varlen(q[0], k[0], v[0], cu, cu, N, causal, 0.1)
+        g1 = attn.bwd(q, k, v, o1, do, l1, causal, 0.1)
+        g2 = attn.bwd_varlen(q[0], k[0], v[0], o2, do[0], l2, cu, cu, N, N, causal, 0.1)
+        torch.cuda.synchronize()
+        assert torch.equal(o1[0], o2) and torch.equal(l1[0], l2)
+        assert all(torch.equal(a[0], b) for a, b in zip(g1, g2))
+
+
+def test_window_of_whole_sequence_equals_no_window():
+    """A window wider than the sequence changes nothing."""
+    say("wide window")
+    H, N, d = 2, 300, 64
+    inp = make_inputs(1, H, N, d, "f16", seed=5)
+    q, k, v = (inp[n][0].cuda() for n in ("q", "k", "v"))
+    cu = torch.tensor([0, N], dtype=torch.int32, device="cuda")
+    o1, l1 = attn.fwd_varlen(q, k, v, cu, cu, N, True, 0.125)
+    o2, l2 = attn.fwd_varlen(q, k, v, cu, cu, N, True, 0.125, window=(N, -1))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
