@@ -5,8 +5,13 @@ the forward (O and lse) and the recompute backward (dQ, dK, dV) of
 B=1, H=32, N=8192, d=128, causal, bf16 attention with inputs resident in HBM.
 
     python bench.py [--steps K] [--warmup W] [--passes fwd|fwdbwd] [--no-cpu-baseline]
+                    [--workload headline|window512|varlen]
 
-Prints one JSON line.  Throughput is algorithmic FLOP/s: forward
+The default (headline) workload is the one above.  `window512` runs the same
+shape with a causal sliding window of 512 keys (local attention, through the
+packed-sequence entry points with one sequence); `varlen` runs a packed batch
+of 16 causal sequences of seeded lengths between 256 and 4096 (32 heads,
+d=128, bf16).  Prints one JSON line.  Throughput is algorithmic FLOP/s: forward
 4*d*pairs, backward 10*d*pairs (five d-deep products per unmasked pair,
 the score recomputation included), pairs = N(N+1)/2 per head when causal.
 Kernel durations come from HIP events recorded on the stream the library
@@ -68,6 +73,99 @@ def cpu_baseline(w, inp, scale, passes, budget_s=10.0):
             "cpu": platform.processor() or platform.machine()}
 
 
+def pairs_window(n, wl):
+    """Unmasked pairs of one causal head of length n whose rows see at most wl + 1 keys."""
+    w = wl + 1
+    return (w * (w + 1)) // 2 + max(0, n - w) * w if n > w else n * (n + 1) // 2
+
+
+class Packed:
+    """A packed-sequence workload timed through attn_fwd_varlen / attn_bwd_varlen."""
+
+    def __init__(self, name, lengths, H, d, dtype, causal, window, seed):
+        import numpy as np
+        import torch
+
+        from io_aware_exact_06_amd.inputs import default_scale, make_inputs
+        self.name, self.H, self.d, self.dtype, self.causal, self.window = name, H, d, dtype, causal, window
+        self.lengths = [int(x) for x in lengths]
+        total = sum(self.lengths)
+        inp = make_inputs(1, H, total, d, dtype, seed, with_dout=True)
+        dev = torch.device("cuda:0")
+        self.q, self.k, self.v, self.do = (inp[n][0].to(dev) for n in ("q", "k", "v", "dout"))
+        cu = np.concatenate([[0], np.cumsum(self.lengths)]).astype(np.int32)
+        self.cu = torch.from_numpy(cu).to(dev)
+        self.scale = default_scale(d)
+        self.maxlen = max(self.lengths)
+        wl = window[0]
+        self.pairs = sum(pairs_window(n, wl) if wl >= 0 else n * (n + 1) // 2 for n in self.lengths) * H
+
+    def run(self, attn, bwd, ev=None):
+        if ev is not None:
+            ev[0].record()
+        o, lse = attn.fwd_varlen(self.q, self.k, self.v, self.cu, self.cu, self.maxlen, self.causal, self.scale,
+                                 self.window)
+        if ev is not None:
+            ev[1].record()
+        if bwd:
+            attn.bwd_varlen(self.q, self.k, self.v, o, self.do, lse, self.cu, self.cu, self.maxlen, self.maxlen,
+                            self.causal, self.scale, self.window)
+            if ev is not None:
+                ev[2].record()
+        return o, lse
+
+
+def bench_packed(args, workload):
+    """Time a packed workload; print its JSON line (same fields as the headline line)."""
+    import numpy as np
+    import torch
+
+    from io_aware_exact_06_amd import attn
+    if workload == "window512":
+        wk = Packed("fwdbwd_B1_H32_N8192_d128_bf16_causal_window512", [8192], 32, 128, "bf16", True, (511, -1),
+                    1003)
+    else:
+        rng = np.random.default_rng(2024)
+        wk = Packed("fwdbwd_H32_varlen16_256to4096_d128_bf16_causal", rng.integers(256, 4097, size=16), 32, 128,
+                    "bf16", True, (-1, -1), 1004)
+    bwd = "bwd" in args.passes
+    for _ in range(args.warmup):
+        wk.run(attn, bwd)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        o, lse = wk.run(attn, bwd, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in evs] if bwd else [0.0]
+    ff = 4.0 * wk.d * wk.pairs
+    fb = 10.0 * wk.d * wk.pairs if bwd else 0.0
+    f_tf = ff / (sum(fwd_ms) / len(fwd_ms) * 1e-3) / 1e12
+    b_tf = fb / (sum(bwd_ms) / len(bwd_ms) * 1e-3) / 1e12 if bwd else None
+    ms_step = wall * 1e3 / args.steps
+    out = {
+        "metric": METRIC, "value": round((ff + fb) / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wk.dtype,
+        "data": "synthetic: iid N(0,1) fp32 rounded to bf16",
+        "config": {"workload": wk.name, "H": wk.H, "d": wk.d, "lengths": wk.lengths, "causal": wk.causal,
+                   "window": list(wk.window), "passes": args.passes, "unmasked_pairs": wk.pairs},
+        "fwd": {"avg_ms": round(sum(fwd_ms) / len(fwd_ms), 4), "tflops": round(f_tf, 2),
+                "pct_peak": round(100 * f_tf / PEAK_BF16_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(b_tf if bwd else f_tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round((b_tf if bwd else f_tf) / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": "attn_bwd_varlen pass" if bwd else "attn_fwd_kernel (packed)"},
+        "outputs_finite": bool(torch.isfinite(o).all()),
+    }
+    if bwd:
+        out["bwd"] = {"avg_ms": round(sum(bwd_ms) / len(bwd_ms), 4), "tflops": round(b_tf, 2),
+                      "pct_peak": round(100 * b_tf / PEAK_BF16_TFLOPS, 2)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -75,6 +173,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--passes", choices=["fwd", "fwdbwd"], default="fwdbwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", choices=["headline", "window512", "varlen"], default="headline")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build runs on a single MI355X; "
@@ -89,6 +188,9 @@ def main():
     if not os.path.exists(attn.LIB_PATH):
         import __graft_entry__
         __graft_entry__.build()
+    if args.workload != "headline":
+        bench_packed(args, args.workload)
+        return
 
     w = WORKLOADS[WORKLOAD_INDEX]
     scale = default_scale(w.d)
