@@ -155,6 +155,23 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, 
                     int window_left, int window_right, float scale, int dtype,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The standard, unfused forward -- a measurement baseline, not a fast path.
+ * It runs the three passes of the hotdry blog's section on the memory
+ * bandwidth bottleneck of traditional attention as three kernels with their
+ * intermediates in device memory: S = scale Q K^T (fp32 [B, H, N, N], the
+ * full matrix even when causal), P = softmax(S) (16-bit [B, H, N, N], causal
+ * entries zero) with lse, then O = P V.  Arguments and outputs as attn_fwd;
+ * `workspace` (16-byte aligned, caller-owned) holds S and P:
+ * attn_fwd_unfused_workspace_bytes(B, H, N) bytes, about 6 N^2 bytes per
+ * head.  B*H <= 65535 and N <= 2^24.  Compared with attn_fwd it shows the
+ * O(N^2) device-memory traffic the fused kernel avoids.
+ */
+size_t attn_fwd_unfused_workspace_bytes(int B, int H, int N);
+int attn_fwd_unfused(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int N, int d, int causal, float scale, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* A static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_string(int status);
 

@@ -23,7 +23,8 @@ STATUS = {
     4: "ATTN_E_ALIGN", 5: "ATTN_E_ALIAS", 6: "ATTN_E_WORKSPACE", 7: "ATTN_E_HIP",
 }
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_string",
-           "attn_fwd_varlen", "attn_bwd_varlen", "attn_bwd_varlen_workspace_bytes")
+           "attn_fwd_varlen", "attn_bwd_varlen", "attn_bwd_varlen_workspace_bytes",
+           "attn_fwd_unfused", "attn_fwd_unfused_workspace_bytes")
 
 _lib = None
 
@@ -58,6 +59,10 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i,
                                       f, i, vp, sz, vp]
         L.attn_bwd_varlen.restype = i
+        L.attn_fwd_unfused_workspace_bytes.argtypes = [i, i, i]
+        L.attn_fwd_unfused_workspace_bytes.restype = sz
+        L.attn_fwd_unfused.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+        L.attn_fwd_unfused.restype = i
         _lib = L
     return _lib
 
@@ -225,3 +230,30 @@ def bwd_varlen(q, k, v, o, dout, lse, cu_q, cu_k, max_seqlen_q: int, max_seqlen_
                            int(window[0]), int(window[1]), scale, _dtype_code(q), workspace.data_ptr(),
                            workspace.numel(), _stream_handle(q.device)))
     return dq, dk, dv
+
+
+def attn_fwd_unfused_workspace_bytes(B, H, N) -> int:
+    return int(lib().attn_fwd_unfused_workspace_bytes(B, H, N))
+
+
+def attn_fwd_unfused(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, workspace, workspace_bytes,
+                     stream) -> int:
+    return lib().attn_fwd_unfused(q, k, v, o, lse, B, H, N, d, int(causal), float(scale), dtype, workspace,
+                                  workspace_bytes, stream)
+
+
+def fwd_unfused(q, k, v, causal: bool = False, scale: float | None = None, o=None, lse=None, workspace=None):
+    """The standard three-pass forward (S and P through device memory); same outputs as fwd."""
+    import torch
+    B, H, N, d = _shape(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    need = attn_fwd_unfused_workspace_bytes(B, H, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(attn_fwd_unfused(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d,
+                            causal, scale, _dtype_code(q), workspace.data_ptr(), workspace.numel(),
+                            _stream_handle(q.device)))
+    return o, lse

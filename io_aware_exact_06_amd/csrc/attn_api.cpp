@@ -168,6 +168,40 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
     return attn::launch_fwd(p) == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 
+size_t attn_fwd_unfused_workspace_bytes(int B, int H, int N) {
+    if (B < 0 || H < 0 || N < 0) return (size_t)-1;
+    if ((int64_t)B * H * N == 0) return 0;
+    if ((int64_t)N > (int64_t)1 << 24 || (int64_t)B * H > 65535) return (size_t)-1;
+    return attn::unfused_workspace_bytes(B, H, N);
+}
+
+int attn_fwd_unfused(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                     int causal, float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    int64_t rows = 0, elems = 0;
+    int st = check_common(B, H, N, d, causal, scale, dtype, &rows, &elems);
+    if (st != ATTN_OK) return st;
+    if (rows == 0) return ATTN_OK;
+    if ((int64_t)B * H > 65535 || (int64_t)N > (int64_t)1 << 24 || rows > INT32_MAX) return ATTN_E_SHAPE;
+    if (!q || !k || !v || !o || !lse) return ATTN_E_NULL;
+    if (!workspace) return ATTN_E_WORKSPACE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+        !aligned(workspace, 16))
+        return ATTN_E_ALIGN;
+    const size_t need = attn::unfused_workspace_bytes(B, H, N);
+    if (workspace_bytes < need) return ATTN_E_WORKSPACE;
+    const size_t tb = (size_t)elems * 2, lb = (size_t)rows * 4;
+    const Range ins[] = {range_of(q, tb), range_of(k, tb), range_of(v, tb)};
+    const Range outs[] = {range_of(o, tb), range_of(lse, lb), range_of(workspace, need)};
+    for (int i = 0; i < 3; ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r)) return i == 2 ? ATTN_E_WORKSPACE : ATTN_E_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], outs[j])) return j == 2 ? ATTN_E_WORKSPACE : ATTN_E_ALIAS;
+    }
+    attn::UnfusedParams p{q, k, v, o, lse, workspace, B, H, N, d, causal, dtype, scale, stream};
+    return attn::launch_unfused(p) == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
 size_t attn_bwd_varlen_workspace_bytes(int H, int total_q) {
     if (H < 0 || total_q < 0) return (size_t)-1;
     if ((int64_t)H * total_q == 0) return 0;

@@ -70,7 +70,30 @@ inline size_t bwd_workspace_bytes_rows(int64_t rows) {
     return (((size_t)rows * sizeof(float)) + 255) & ~(size_t)255;
 }
 
+// The unfused three-pass baseline (S and P in the caller's workspace).
+struct UnfusedParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    void* workspace;
+    int B, H, N, d, causal, dtype;
+    float scale;
+    void* stream;
+};
+
+// Workspace of the unfused baseline: fp32 S [BH, N, N], then 16-bit P [BH, N, N],
+// each region rounded up to 256 bytes.
+inline size_t unfused_score_bytes(int64_t B, int64_t H, int64_t N) {
+    return (((size_t)(B * H * N) * (size_t)N * 4) + 255) & ~(size_t)255;
+}
+inline size_t unfused_workspace_bytes(int64_t B, int64_t H, int64_t N) {
+    return unfused_score_bytes(B, H, N) + ((((size_t)(B * H * N) * (size_t)N * 2) + 255) & ~(size_t)255);
+}
+
 hipError_t launch_fwd(const FwdParams& p);
+hipError_t launch_unfused(const UnfusedParams& p);
 hipError_t launch_bwd(const BwdParams& p);
 
 }  // namespace attn

@@ -143,3 +143,22 @@ def test_bwd_varlen_workspace_and_rejects():
     assert call(ws=A + 0x900000) == 6
     assert call(max_k=-1) == 2
     assert call(q=0, k=0, v=0, o=0, dout=0, lse=0, dq=0, dk=0, dv=0, tq=0, tk=0) == 0
+
+
+def test_fwd_unfused_validation():
+    B, H, N, d = 1, 2, 64, 64
+    need = attn.attn_fwd_unfused_workspace_bytes(B, H, N)
+    assert need >= B * H * N * N * 6 and need % 256 == 0
+    assert attn.attn_fwd_unfused_workspace_bytes(1, 1 << 17, 4) == ctypes.c_size_t(-1).value
+    base = dict(q=A, k=A + 0x100000, v=A + 0x200000, o=A + 0x300000, lse=A + 0x400000, ws=A + 0x500000)
+
+    def call(ws_bytes=need, **kw):
+        a = dict(base)
+        a.update(kw)
+        return attn.attn_fwd_unfused(a["q"], a["k"], a["v"], a["o"], a["lse"], B, H, N, d, 1, 0.125, 1, a["ws"],
+                                     ws_bytes, None)
+    assert call(ws=0) == 6
+    assert call(ws_bytes=need - 1) == 6
+    assert call(ws=A + 0x500004) == 4
+    assert call(o=A + 0x200000) == 5
+    assert call(ws=A + 0x300000) == 6
