@@ -5,13 +5,17 @@ the forward (O and lse) and the recompute backward (dQ, dK, dV) of
 B=1, H=32, N=8192, d=128, causal, bf16 attention with inputs resident in HBM.
 
     python bench.py [--steps K] [--warmup W] [--passes fwd|fwdbwd] [--no-cpu-baseline]
-                    [--workload headline|window512|varlen]
+                    [--workload headline|window512|varlen|io] [--n N]
 
 The default (headline) workload is the one above.  `window512` runs the same
 shape with a causal sliding window of 512 keys (local attention, through the
 packed-sequence entry points with one sequence); `varlen` runs a packed batch
 of 16 causal sequences of seeded lengths between 256 and 4096 (32 heads,
-d=128, bf16).  Prints one JSON line.  Throughput is algorithmic FLOP/s: forward
+d=128, bf16).  `io` times the fused forward against the unfused three-pass
+forward (B=1, H=8, N=--n, d=128, bf16, causal) and runs one plain 1 GiB device
+copy; run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE it gives each kernel's
+memory traffic, the copy serving as the counters' calibration.  Prints one
+JSON line.  Throughput is algorithmic FLOP/s: forward
 4*d*pairs, backward 10*d*pairs (five d-deep products per unmasked pair,
 the score recomputation included), pairs = N(N+1)/2 per head when causal.
 Kernel durations come from HIP events recorded on the stream the library
@@ -34,6 +38,29 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense 16-bit MFMA FLOP/clk/CU
 WORKLOAD_INDEX = 3         # B=1 H=32 N=8192 d=128 bf16 causal, forward + backward
 METRIC = "fused attention fwd/bwd TFLOP/s and % MFMA peak, N=8192 d=128 causal bf16"
+
+# HBM bytes per launch of the headline kernels, from two rocprofv3 --pmc passes
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) of `bench.py --no-cpu-baseline
+# --steps 3 --warmup 1`, scaled by what the same counters read for a plain 1 GiB
+# device copy (FETCH_SIZE reads half the copied bytes: factor 2.0; WRITE_SIZE
+# reads them exactly: factor 1.0).  The figures hold only for the kernel
+# sources they were taken on, whose SHA-256 is stored beside them; for any
+# other sources the traffic is reported as null.
+TRAFFIC_SOURCES = ("attn_device.h", "attn_launch.h", "attn_fwd.hip", "attn_bwd.hip")
+TRAFFIC = {
+    "sha256": "406773809a5f85864da4a0310f662a41905a45d75594e41a356ab9c889b69bcd",
+    "fwd": 288819200,             # attn_fwd_kernel: fetch 2 x 107745.0 KiB + write 66560.0 KiB
+    "bwd": 479659622 + 409856819,  # attn_bwd_dq_kernel (2 x 199911.5 + 68594.6 KiB) + attn_bwd_dkdv_kernel (2 x 134589.4 + 131072.0 KiB)
+}
+
+
+def measured_traffic(which):
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "io_aware_exact_06_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return TRAFFIC[which] if h.hexdigest() == TRAFFIC["sha256"] else None
 
 
 def flops(w, passes):
@@ -166,6 +193,43 @@ def bench_packed(args, workload):
     print(json.dumps(out), flush=True)
 
 
+def bench_io(args):
+    """Fused vs unfused forward at one sequence length, plus a calibration copy."""
+    import torch
+
+    from io_aware_exact_06_amd import attn
+    from io_aware_exact_06_amd.inputs import default_scale, make_inputs
+    B, H, N, d = 1, 8, args.n, 128
+    inp = make_inputs(B, H, N, d, "bf16", 1005)
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    scale = default_scale(d)
+    ws = torch.empty(attn.attn_fwd_unfused_workspace_bytes(B, H, N), dtype=torch.uint8, device=dev)
+    res = {}
+    for name, fn in (("fused", lambda: attn.fwd(q, k, v, True, scale)),
+                     ("unfused", lambda: attn.fwd_unfused(q, k, v, True, scale, workspace=ws))):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            o, lse = fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = {"avg_ms": round(e0.elapsed_time(e1) / args.steps, 4), "finite": bool(torch.isfinite(o).all())}
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)  # calibration: exactly 1 GiB read and 1 GiB written
+    torch.cuda.synchronize()
+    pairs = N * (N + 1) // 2 * B * H
+    compulsory = 4 * B * H * N * d * 2 + B * H * N * 4
+    print(json.dumps({"workload": "io_B1_H8_N%d_d128_bf16_causal" % N, "N": N, "unmasked_pairs": pairs,
+                      "compulsory_bytes_fused": compulsory,
+                      "intermediate_bytes_unfused": B * H * N * N * (4 + 2), "fused": res["fused"],
+                      "unfused": res["unfused"], "calibration_copy_bytes": 1 << 30}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -173,7 +237,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--passes", choices=["fwd", "fwdbwd"], default="fwdbwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=["headline", "window512", "varlen"], default="headline")
+    ap.add_argument("--workload", choices=["headline", "window512", "varlen", "io"], default="headline")
+    ap.add_argument("--n", type=int, default=4096, help="sequence length of the io workload")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build runs on a single MI355X; "
@@ -188,6 +253,9 @@ def main():
     if not os.path.exists(attn.LIB_PATH):
         import __graft_entry__
         __graft_entry__.build()
+    if args.workload == "io":
+        bench_io(args)
+        return
     if args.workload != "headline":
         bench_packed(args, args.workload)
         return
@@ -239,13 +307,15 @@ def main():
     # Dominant work: the backward pass (attn_bwd_dq_kernel then attn_bwd_dkdv_kernel,
     # timed together by the events around one attn_bwd call) when it runs, else the forward.
     fwd_roof = {"bound": "mfma", "achieved": round(f_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(f_tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": "attn_fwd_kernel",
+                "frac": round(f_tf / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic("fwd"),
+                "kernel": "attn_fwd_kernel",
                 "avg_ms": round(sum(fwd_ms) / len(fwd_ms), 4)}
     if bwd:
         dom = {"kernel": "attn_bwd pass: attn_bwd_dq_kernel + attn_bwd_dkdv_kernel",
-               "achieved": b_tf, "avg_ms": sum(bwd_ms) / len(bwd_ms)}
+               "achieved": b_tf, "avg_ms": sum(bwd_ms) / len(bwd_ms), "traffic": measured_traffic("bwd")}
     else:
-        dom = {"kernel": "attn_fwd_kernel", "achieved": f_tf, "avg_ms": sum(fwd_ms) / len(fwd_ms)}
+        dom = {"kernel": "attn_fwd_kernel", "achieved": f_tf, "avg_ms": sum(fwd_ms) / len(fwd_ms),
+               "traffic": measured_traffic("fwd")}
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -265,7 +335,7 @@ def main():
                 "tflops": round(f_tf, 2), "pct_peak": round(100 * f_tf / PEAK_BF16_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(dom["achieved"], 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(dom["achieved"] / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": dom["kernel"], "avg_ms": round(dom["avg_ms"], 4)},
+                     "traffic": dom["traffic"], "kernel": dom["kernel"], "avg_ms": round(dom["avg_ms"], 4)},
         "roofline_fwd": fwd_roof,
         "outputs_finite": finite,
     }
