@@ -1,44 +1,42 @@
 // attn_fwd.hip -- fused exact-attention forward for gfx950.
 //
-// One work group owns BQ query rows of one (batch, head): four waves, each
-// owning QB blocks of 32 rows.  The group streams the keys and values in
-// tiles of BK = 64 rows through LDS (double-buffered; the next tile is
-// prefetched into registers while the current one is consumed), and each
-// wave keeps, for its rows, the running maximum m, the running sum l and the
-// partial output in registers: the online softmax of the hotdry blog's
-// section "3. 在线softmax算法" (initialise m = -inf and l = 0; for every key
-// block raise the maximum, rescale the running sum and the partial output
-// when it grew, add the block's exponentials and their weighted values).
-// Only O and lse = scale * m + ln l leave the chip (section "1. 内核融合策略":
-// write only the final output; section "4. 重计算" keeps one statistic per
-// row).
+// One work group owns 128 query rows of one sequence (of one head): four
+// waves of 32 rows (QB blocks of 32 rows per wave in general).  Keys and values stream through LDS in tiles of 64 rows,
+// double-buffered and loaded by the DMA path (global_load_lds: global memory
+// straight into LDS, no registers); each wave keeps, for its rows, the
+// running maximum m, the running sum l and the partial output in registers:
+// the online softmax of the hotdry blog's section "3. 在线softmax算法"
+// (initialise m = -inf and l = 0; for every key block raise the maximum,
+// rescale the running sum and the partial output when it grew, add the
+// block's exponentials and their weighted values).  Only O and
+// lse = scale * m + ln l leave the chip (section "1. 内核融合策略": write only
+// the final output; section "4. 重计算" keeps one statistic per row).
 //
 // Orientation: every product is computed transposed, S^T = K Q^T and
-// O^T = V^T P^T, on the 32x32x16 MFMA.  In that orientation accumulator lane
-// l always belongs to query row l % 32 of its block, so the row maximum, row
-// sum and rescale factor are per-lane scalars; the only cross-lane step is
-// one exchange between lane l and lane l ^ 32, which hold the two halves of
-// the same row.  The exponentials leave the S^T accumulator directly as the B
-// operand of the P.V product (the key order inside an MFMA k-step is free, so
-// the accumulator's own order is used), and V^T is read from the row-major V
-// tile with the LDS transpose read.  Each K fragment and V^T fragment read
-// from LDS feeds QB MFMAs (one per query block): LDS bandwidth per flop falls
-// as 1/QB.
+// O^T = V^T P^T, on the 32x32x16 MFMA, so that accumulator lane l belongs to
+// query row l % 32: the row maximum, the row sum and the rescale factor are
+// per-lane scalars, and the only cross-lane step is one exchange between
+// lanes l and l ^ 32.  The exponentials leave the S^T accumulator directly as
+// the B operand of the P.V product, and V^T is read from the V tile with the
+// LDS transpose read.
 //
-// Causal masking (snabindia chapter 1: the causal call skips the upper
-// triangle): key tiles beyond the group's last row are never loaded; a query
-// block skips a loaded tile that lies wholly above its rows; only tiles that
-// cross the diagonal or the end of the sequence are masked element by element.
+// Software pipeline (per wave): while the matrix cores compute the scores of
+// key tile j+1, the vector unit turns the scores of tile j into P (exp,
+// running sum, packing); then the P.V products of tile j run.  Independent
+// MFMA and VALU work of one wave overlap on the SIMD.
+//
+// Rescaling: the maximum m used for the exponentials is raised only when a
+// row's new maximum exceeds it by more than 2^8 in the exponent (exp2 units);
+// otherwise exponentials up to 2^8 are accumulated against the old m.  The
+// online-softmax identity holds for any m the row uses consistently, so the
+// result is the same up to rounding, and most tiles skip the rescale.
+//
+// Causal and window masking (snabindia chapter 1: the causal call skips the
+// upper triangle): key tiles no row of the group sees are never loaded; only
+// tiles at the edge of the visible band are masked element by element.
 
 #include "attn_device.h"
 #include "attn_launch.h"
-
-// Query blocks (of 32 rows) per wave.  One block per wave, two waves per SIMD,
-// measured fastest: with two blocks per wave (one wave per SIMD) the loop
-// spills registers and loses the second wave's latency hiding.
-#ifndef ATTN_FWD_QB
-#define ATTN_FWD_QB 1
-#endif
 
 namespace attn {
 
@@ -46,19 +44,98 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kBK = 64;  // key rows per tile
+constexpr int kBK = 64;        // key rows per tile
+// Query blocks (of 32 rows) per wave.  One block per wave with two waves per
+// SIMD measured fastest: two blocks per wave halve the LDS reads per MFMA but
+// need the output accumulators in AGPRs at one wave per SIMD, where the
+// compiler also places the score accumulators and copies them back for the
+// vector unit.
+#ifndef ATTN_FWD_QB
+#define ATTN_FWD_QB 1
+#endif
+constexpr float kLazy = 8.0f;  // rescale only when the maximum grows by more than 2^8
 
-template <int D, int QB>
-struct FwdShape {
-    static constexpr int BQ = kWaves * 32 * QB;       // query rows per work group
-    static constexpr int KS = D / 16;                 // MFMA k-steps of S^T over d
-    static constexpr int DB = D / 32;                 // 32-row blocks of O^T
-    static constexpr int KB = kBK / 32;               // 32-key blocks of a tile
-    static constexpr int STR = LdsStride<D>::value;   // LDS row stride in elements
-    static constexpr int CH = D / 8;                  // 16-byte chunks per row
-    static constexpr int TILE = kBK * STR;            // elements per LDS tile
-    static_assert(BQ * STR <= 4 * TILE, "output staging must fit in the tile buffers");
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS image of a 64 x D tile written by the DMA path.  The tile is cut into
+// blocks of 16 rows x 4 chunks (a chunk is 8 values, 16 bytes); block
+// (rg, cg) sits at byte (rg * CG + cg) * 1024, CG = D / 32.  Inside a block,
+// row r takes 64 bytes at r * 64 and its chunk c is stored in slot
+// c ^ ((r >> 2) & 3).  One wave-wide DMA instruction fills one block (lane L
+// writes bytes 16 L .. 16 L + 15, i.e. row L / 4, slot L % 4), so every
+// global read is 16 rows x 64 contiguous bytes.  The slot swizzle makes both
+// LDS read patterns conflict-free: 16 lanes reading one chunk of 16
+// consecutive rows (128-bit reads) and 16 lanes reading 4 rows x 32 bytes
+// (transpose reads) each touch 16 distinct bank groups.
+template <int D>
+struct DmaTile {
+    static constexpr int CG = D / 32;          // chunk groups per row
+    static constexpr int BYTES = kBK * D * 2;  // one tile
+    static constexpr int PER_WAVE = CG;        // blocks (DMA instructions) per wave per tile
+
+    // Byte offset, inside this lane's global tile, of the chunk it loads for
+    // the block of chunk group cg of row group rg (excluding the block's base).
+    __device__ static inline uint32_t lane_goff(int lane) {
+        const int r = lane >> 2, c = (lane & 3) ^ ((r >> 2) & 3);
+        return (uint32_t)(r * D + c * 8) * 2u;
+    }
+    // Block b of a tile handled by wave w in its i-th instruction.
+    __device__ static inline int block(int w, int i) { return w + kWaves * i; }
 };
+
+// One DMA instruction: 16 bytes per lane from sbase + voff (global) into LDS
+// at lds + 16 * lane.  Issued in assembly: the compiler does not track it,
+// so it neither waits for it before unrelated LDS reads nor reuses LDS
+// values across it ("memory" clobber); the kernel waits for completion with
+// wait_dma() and a barrier before any wave reads the tile.  M0 carries the
+// LDS address and needs one wait state after being written.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ inline void dma16(const void* base, uint32_t voff, uint32_t lds_byte) {
+    // base and lds_byte are wave-uniform; make that explicit for the SGPR operands
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const uint64_t sb = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b) |
+                        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32);
+    const void* sbase = (const void*)(uintptr_t)sb;
+    const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane(lds_byte);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ inline uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Issue the DMA of key/value rows r0 .. r0+63 of a [nrows, D] array into an
+// LDS tile.  Rows at or beyond nrows read row nrows-1 (callers mask them).
+// w is the (wave-uniform) wave index.
+template <int D>
+__device__ inline void dma_tile(const uint16_t* __restrict__ src, int r0, int nrows, const uint16_t* lds_tile, int w,
+                                int lane, uint32_t goff) {
+    using DT = DmaTile<D>;
+    const char* base = (const char*)(src + (int64_t)r0 * D);
+    const uint32_t lt = lds_addr(lds_tile);
+    if (r0 + kBK <= nrows) {
+#pragma unroll
+        for (int i = 0; i < DT::PER_WAVE; ++i) {
+            const int b = DT::block(w, i), rg = b / DT::CG, cg = b % DT::CG;
+            dma16(base + (rg * 16 * D + cg * 32) * 2, goff, lt + b * 1024);
+        }
+    } else {
+        const int r = lane >> 2, c = (lane & 3) ^ ((r >> 2) & 3);
+#pragma unroll
+        for (int i = 0; i < DT::PER_WAVE; ++i) {
+            const int b = DT::block(w, i), rg = b / DT::CG, cg = b % DT::CG;
+            const int row = min(rg * 16 + r, nrows - 1 - r0);
+            dma16(base, (uint32_t)(row * D + cg * 32 + c * 8) * 2u, lt + b * 1024);
+        }
+    }
+}
+
+__device__ inline void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0); expcnt, lgkmcnt not waited on
 
 template <class T, int D, int QB>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
@@ -66,191 +143,241 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
 void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                      float* __restrict__ LSE, SeqLayout L, int ntq, float scale, float c) {
-    using S = FwdShape<D, QB>;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * S::TILE];
-    uint16_t* const Ks = smem;               // two K tiles
-    uint16_t* const Vs = smem + 2 * S::TILE;  // two V tiles
+    using DT = DmaTile<D>;
+    constexpr int KS = D / 16;                 // MFMA k-steps of S^T over d
+    constexpr int DB = D / 32;                 // 32-row blocks of O^T
+    constexpr int TB = DT::BYTES / 2;          // tile size in 16-bit elements
+    constexpr int STR = LdsStride<D>::value;   // row stride of the output staging
+    constexpr int CH = D / 8;
+    constexpr int BQ = kWaves * 32 * QB;       // query rows per work group
+    constexpr int SMEM = (BQ * STR > 4 * TB) ? BQ * STR : 4 * TB;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM];
+    uint16_t* const Kb = smem;           // K tiles: buffers 0, 1
+    uint16_t* const Vb = smem + 2 * TB;  // V tiles: buffers 0, 1
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n32 = lane & 31, h = lane >> 5;
 
-    // Work item: (sequence, query tile).  Each XCD gets a contiguous range;
-    // when rows see only keys up to a right bound (causal), tiles run longest
-    // first.
     const int item = xcd_contiguous(blockIdx.x, gridDim.x);
     const Seq sq = resolve(L, item / ntq);
     const int qt = (L.wr >= 0 && L.wl < 0) ? ntq - 1 - item % ntq : item % ntq;
-    const int q0 = qt * S::BQ;
+    const int q0 = qt * BQ;
     if (q0 >= sq.nq) return;  // the whole group: no barrier has been reached
     const int nq = sq.nq, nk = sq.nk;
     const uint16_t* Qh = Q + sq.qrow0 * D;
     const uint16_t* Kh = K + sq.krow0 * D;
     const uint16_t* Vh = V + sq.krow0 * D;
-    const int wq0 = q0 + w * 32 * QB;  // first row of this wave; block qb starts at wq0 + 32 qb
+    const int wq0 = q0 + w * 32 * QB;  // block qb of this wave starts at row wq0 + 32 qb
 
     // Q^T fragments (B operand of S^T = K Q^T), resident for the whole loop.
-    // Rows past the end read row nq-1; their outputs are never stored.
-    u32x4 qf[QB][S::KS];
+    u32x4 qf[QB][KS];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int qrow = min(wq0 + 32 * qb + n32, nq - 1);
 #pragma unroll
-        for (int ks = 0; ks < S::KS; ++ks) qf[qb][ks] = *(const u32x4*)(Qh + (int64_t)qrow * D + 16 * ks + 8 * h);
+        for (int ks = 0; ks < KS; ++ks) qf[qb][ks] = *(const u32x4*)(Qh + (int64_t)qrow * D + 16 * ks + 8 * h);
     }
 
-    // Key tiles some row of the group sees, and those every row sees in full
-    // (which run without any per-element test).
-    const int qlast = min(q0 + S::BQ, nq) - 1;
+    const int qlast = min(q0 + BQ, nq) - 1;
     const TileRange tr = tile_range(sq.key_lo(q0), sq.key_hi(qlast), sq.key_lo(qlast),
                                     min(sq.key_hi(q0), nk - 1), nk, kBK);
 
-    TileCopy<kBK, D, kThreads> kc(tid), vc(tid);
-    if (tr.end > tr.first) {
-        const int b0 = (tr.first & 1) * S::TILE;
-        kc.load(Kh, tr.first * kBK, nk, tid);
-        vc.load(Vh, tr.first * kBK, nk, tid);
-        kc.store(Ks + b0);
-        vc.store(Vs + b0);
+    // Per-lane LDS read offsets (bytes, relative to a tile):
+    //  K fragment of k-step ks, key block kb: row kb*32 + n32, chunk 2 ks + h
+    //    -> kofs[ks & 1] + (2 kb * CG + ks / 2) * 1024 (the n32 / 16 row group folded in);
+    //  V^T transpose read e (rows 8 e + 4 h + g16 / 4 of a 16-row step), 32-column block db
+    //    -> vofs[e] + ((2 kb + t) * CG + db) * 1024.
+    uint32_t kofs[2], vofs[2];
+    {
+        const int r = n32 & 15, q = (r >> 2) & 3;
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+            kofs[p] = (uint32_t)((n32 >> 4) * DT::CG * 1024 + r * 64 + (((2 * p + h) ^ q) << 4));
+        const int g16 = lane & 15, x = (lane >> 4) & 1;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int row = 8 * e + 4 * h + (g16 >> 2);
+            const int cc = 2 * x + ((g16 & 3) >> 1);
+            vofs[e] = (uint32_t)(row * 64 + ((cc ^ (2 * e + h)) << 4) + (g16 & 1) * 8);
+        }
     }
-    __syncthreads();
+    const uint32_t goff = DT::lane_goff(lane);
 
-    f32x16 oacc[QB][S::DB];
+    f32x16 oacc[QB][DB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int db = 0; db < S::DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int e = 0; e < 16; ++e) oacc[qb][db][e] = 0.f;
-    float m[QB], l[QB];  // running raw-score maximum; this lane's share of the running sum
+    float m[QB], l[QB];  // running maximum (raw score); this lane's share of the running sum
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         m[qb] = kNegInf;
         l[qb] = 0.f;
     }
+    f32x16 sacc[2][QB][2];  // scores of the tiles with even / odd index: [parity][query block][key block]
 
-    const int tr_off = tr_lane_offset<S::STR>(lane);  // V^T read transposed from the V tile
+    // S^T(jt) = K(jt) Q^T into sacc[PAR], K(jt) in K buffer PAR.  Each K
+    // fragment read from LDS feeds QB MFMAs.
+    auto scores = [&](auto par_tag) __attribute__((always_inline)) {
+        constexpr int PAR = decltype(par_tag)::value;
+        const char* kt = (const char*)(Kb + PAR * TB);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) sacc[PAR][qb][kb][e] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const u32x4 a = *(const u32x4*)(kt + kofs[ks & 1] + (2 * kb * DT::CG + ks / 2) * 1024);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) sacc[PAR][qb][kb] = mfma32<T>(a, qf[qb][ks], sacc[PAR][qb][kb]);
+            }
+    };
 
-    // One key tile.  MASKED tiles (the diagonal of a causal group, the ragged
-    // end of the sequence) mask scores element by element; the others run
-    // without any per-element test.
-    auto step = [&](int jt, auto masked_tag) {
+    // Prologue: tiles first (K, V) and first+1 (K) in flight, then the scores of the first.
+    if (tr.end > tr.first) {
+        dma_tile<D>(Kh, tr.first * kBK, nk, Kb + (tr.first & 1) * TB, w, lane, goff);
+        dma_tile<D>(Vh, tr.first * kBK, nk, Vb + (tr.first & 1) * TB, w, lane, goff);
+        if (tr.first + 1 < tr.end)
+            dma_tile<D>(Kh, (tr.first + 1) * kBK, nk, Kb + ((tr.first + 1) & 1) * TB, w, lane, goff);
+    }
+    // Unconditional: the Q fragments and the first tiles have landed.  The
+    // compiler counts only its own loads in vmcnt; waiting for everything
+    // here keeps it from placing partial waits on the Q fragments inside the
+    // loop, where the hardware counter also holds the prefetch DMA.
+    wait_dma();
+    __syncthreads();
+    if (tr.end > tr.first) {
+        if (tr.first & 1) scores(Flag<1>{});
+        else scores(Flag<0>{});
+    }
+
+    // One key tile jt (parity PAR): its scores are in sacc[PAR]; K(jt+1) and
+    // V(jt) are in LDS.  MASKED: the tile crosses the edge of some row's
+    // visible band.  NEXT: a tile jt+1 exists.
+    auto step = [&](int jt, auto par_tag, auto masked_tag, auto next_tag) __attribute__((always_inline)) {
+        constexpr int PAR = decltype(par_tag)::value;
         constexpr bool MASKED = decltype(masked_tag)::value;
-        const int buf = (jt & 1) * S::TILE;
+        constexpr bool NEXT = decltype(next_tag)::value;
         const int k0 = jt * kBK;
-        const bool more = jt + 1 < tr.end;
-        if (more) {
-            kc.load(Kh, k0 + kBK, nk, tid);
-            vc.load(Vh, k0 + kBK, nk, tid);
+        // Every wave has finished tile jt-1 (the K(jt) and V(jt-1) buffers
+        // are free) and the DMA of K(jt+1), V(jt) has landed.
+        __syncthreads();
+        if (NEXT) {
+            if (jt + 2 < tr.end) dma_tile<D>(Kh, k0 + 2 * kBK, nk, Kb + PAR * TB, w, lane, goff);
+            dma_tile<D>(Vh, k0 + kBK, nk, Vb + (1 - PAR) * TB, w, lane, goff);
         }
-        // Query blocks of this wave that see at least one key of the tile.
-        bool act[QB];
-        bool any = false;
+        float mc[QB];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            const int r0 = wq0 + 32 * qb;
-            act[qb] = !MASKED || (r0 < nq && k0 <= sq.key_hi(r0 + 31) && k0 + kBK - 1 >= sq.key_lo(r0));
-            any = any || act[qb];
-        }
-        if (any) {
-            // ---- S^T = K Q^T: each K fragment feeds every active query block
-            f32x16 s[QB][S::KB];
+            f32x16(&s)[2] = sacc[PAR][qb];
+            if constexpr (MASKED) {
+                const int qrow = wq0 + 32 * qb + n32;
+                const int klo = sq.key_lo(qrow), khi = min(sq.key_hi(qrow), nk - 1);
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                for (int kb = 0; kb < S::KB; ++kb)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) s[qb][kb][e] = 0.f;
-            prio_mfma();
-#pragma unroll
-            for (int kb = 0; kb < S::KB; ++kb) {
-                const uint16_t* kp = Ks + buf + (kb * 32 + n32) * S::STR + 8 * h;
-#pragma unroll
-                for (int ks = 0; ks < S::KS; ++ks) {
-                    const u32x4 a = *(const u32x4*)(kp + 16 * ks);
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb)
-                        if (act[qb]) s[qb][kb] = mfma32<T>(a, qf[qb][ks], s[qb][kb]);
-                }
-            }
-            sched_reads_ahead<4, S::KB * S::KS * QB, 1>();
-            prio_normal();
-            u32x4 pf[QB][S::KB][2];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                if (!act[qb]) continue;
-                if constexpr (MASKED) {
-                    // ---- mask keys past the end and keys outside the row's window
-                    const int qrow = wq0 + 32 * qb + n32;
-                    const int klo = sq.key_lo(qrow), khi = min(sq.key_hi(qrow), nk - 1);
-#pragma unroll
-                    for (int kb = 0; kb < S::KB; ++kb)
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) {
-                            const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-                            if (key < klo || key > khi) s[qb][kb][e] = kNegInf;
-                        }
-                }
-                // ---- online softmax: raise the maximum, rescale when it grew
-                float mx = s[qb][0][0];
-#pragma unroll
-                for (int kb = 0; kb < S::KB; ++kb)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[qb][kb][e]);
-                mx = max_with_other_half(mx);
-                const float mnew = fmaxf(m[qb], mx);
-                if (__any(mnew > m[qb])) {
-                    const float alpha = (m[qb] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((m[qb] - mnew) * c);
-                    l[qb] *= alpha;
-#pragma unroll
-                    for (int db = 0; db < S::DB; ++db)
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) oacc[qb][db][e] *= alpha;
-                }
-                m[qb] = mnew;
-                const float mc = (mnew == kNegInf) ? 0.f : mnew * c;
-                // ---- P^T = exp2(c*s - c*m), packed as the B operand of O^T += V^T P^T
-#pragma unroll
-                for (int kb = 0; kb < S::KB; ++kb) {
-                    f32x16 p;
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
-                        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][e], c, -mc));
-                        if constexpr (MASKED) pe = s[qb][kb][e] == kNegInf ? 0.f : pe;
-                        l[qb] += pe;  // the running sum adds the fp32 exponentials
-                        p[e] = pe;
+                        const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+                        if (key < klo || key > khi) s[kb][e] = kNegInf;
                     }
-                    pack_acc_as_b<T>(p, pf[qb][kb][0], pf[qb][kb][1]);
-                }
             }
-            // ---- O^T += V^T P^T: each V^T fragment feeds every active query block
-            const uint16_t* vp = Vs + buf + tr_off;
-            prio_mfma();
+            float mx = s[0][0];
 #pragma unroll
-            for (int db = 0; db < S::DB; ++db)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int kb = 0; kb < S::KB; ++kb)
+                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
+            mx = max_with_other_half(mx);
+            // Raise m (and rescale) only when the maximum grew by more than 2^8.
+            const bool grow = mx > m[qb] && (m[qb] == kNegInf || (mx - m[qb]) * c > kLazy);
+            if (__any(grow)) {
+                const float mnew = fmaxf(m[qb], mx);
+                const float alpha = (m[qb] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((m[qb] - mnew) * c);
+                l[qb] *= alpha;
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const u32x4 a = tr_operand<S::STR>(vp, kb * 32 + 16 * t, 32 * db);
+                for (int db = 0; db < DB; ++db)
 #pragma unroll
-                        for (int qb = 0; qb < QB; ++qb)
-                            if (act[qb]) oacc[qb][db] = mfma32<T>(a, pf[qb][kb][t], oacc[qb][db]);
-                    }
-            sched_reads_ahead<8, S::DB * S::KB * 2 * QB, 2>();
-            prio_normal();
+                    for (int e = 0; e < 16; ++e) oacc[qb][db][e] *= alpha;
+                m[qb] = mnew;
+            }
+            mc[qb] = (m[qb] == kNegInf) ? 0.f : m[qb] * c;
         }
-        if (more) {
-            kc.store(Ks + S::TILE - buf);
-            vc.store(Vs + S::TILE - buf);
-        }
-        __syncthreads();
+        // Scores of the next tile on the matrix cores while P of this tile
+        // is formed on the vector unit.
+        if (NEXT) scores(Flag<1 - PAR>{});
+        u32x4 pf[QB][2][2];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const f32x16& sv = sacc[PAR][qb][kb];
+                f32x16 p;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], c, -mc[qb]));
+                    if constexpr (MASKED) pe = sv[e] == kNegInf ? 0.f : pe;
+                    l[qb] += pe;  // the running sum adds the fp32 exponentials
+                    p[e] = pe;
+                }
+                pack_acc_as_b<T>(p, pf[qb][kb][0], pf[qb][kb][1]);
+            }
+        // O^T += V^T P^T: each V^T fragment read from LDS feeds QB MFMAs
+        const char* vt = (const char*)(Vb + PAR * TB);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const int blk = ((2 * kb + t) * DT::CG + db) * 1024;
+                    const u32x2 lo = __builtin_bit_cast(
+                        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + vofs[0] + blk)));
+                    const u32x2 hi = __builtin_bit_cast(
+                        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + vofs[1] + blk)));
+                    const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32<T>(a, pf[qb][kb][t], oacc[qb][db]);
+                }
+        wait_dma();
     };
-    for (int jt = tr.first; jt < tr.full_first; ++jt) step(jt, Flag<true>{});
-    for (int jt = tr.full_first; jt < tr.full_end; ++jt) step(jt, Flag<false>{});
-    for (int jt = tr.full_end; jt < tr.end; ++jt) step(jt, Flag<true>{});
+
+    // Tiles [a, b) all of one kind (masked or not), none of them the last.
+    auto run = [&](int a, int b, auto masked_tag) __attribute__((always_inline)) {
+        int jt = a;
+        if (jt < b && (jt & 1)) {
+            step(jt, Flag<1>{}, masked_tag, Flag<true>{});
+            ++jt;
+        }
+        for (; jt + 1 < b; jt += 2) {
+            step(jt, Flag<0>{}, masked_tag, Flag<true>{});
+            step(jt + 1, Flag<1>{}, masked_tag, Flag<true>{});
+        }
+        if (jt < b) step(jt, Flag<0>{}, masked_tag, Flag<true>{});
+    };
+    if (tr.end > tr.first) {
+        const int last = tr.end - 1;
+        run(tr.first, min(tr.full_first, last), Flag<true>{});
+        run(tr.full_first, min(tr.full_end, last), Flag<false>{});
+        run(max(tr.full_end, tr.full_first), last, Flag<true>{});
+        const bool last_masked = last < tr.full_first || last >= tr.full_end;
+        if (last & 1) {
+            if (last_masked) step(last, Flag<1>{}, Flag<true>{}, Flag<false>{});
+            else step(last, Flag<1>{}, Flag<false>{}, Flag<false>{});
+        } else {
+            if (last_masked) step(last, Flag<0>{}, Flag<true>{}, Flag<false>{});
+            else step(last, Flag<0>{}, Flag<false>{}, Flag<false>{});
+        }
+    }
+    __syncthreads();  // every wave is done with the tile buffers
 
     // ---- epilogue: O = O^T / l, staged through LDS for row-contiguous stores
-    uint16_t* Os = smem;  // the loop ended on a barrier: every tile buffer is free
+    uint16_t* Os = smem;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int qrow = wq0 + 32 * qb + n32;
@@ -258,9 +385,9 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         // a row that sees no key at all: O = 0, lse = -inf
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         if (h == 0 && qrow < nq) LSE[sq.qrow0 + qrow] = lt > 0.f ? m[qb] * scale + logf(lt) : kNegInf;
-        const int orow = (w * 32 * QB + 32 * qb + n32) * S::STR;
+        const int orow = (w * 32 * QB + 32 * qb + n32) * STR;
 #pragma unroll
-        for (int db = 0; db < S::DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 u32x2 pk = {pack2<T>(oacc[qb][db][4 * g] * inv, oacc[qb][db][4 * g + 1] * inv),
@@ -270,16 +397,16 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     }
     __syncthreads();
     uint16_t* Oh = O + sq.qrow0 * D;
-    for (int ch = tid; ch < S::BQ * S::CH; ch += kThreads) {
-        const int r = ch / S::CH, col = ch % S::CH;
-        if (q0 + r < nq) *(u32x4*)(Oh + (int64_t)(q0 + r) * D + 8 * col) = *(const u32x4*)(Os + r * S::STR + 8 * col);
+    for (int ch = tid; ch < BQ * CH; ch += kThreads) {
+        const int r = ch / CH, col = ch % CH;
+        if (q0 + r < nq) *(u32x4*)(Oh + (int64_t)(q0 + r) * D + 8 * col) = *(const u32x4*)(Os + r * STR + 8 * col);
     }
 }
 
-template <class T, int D, int QB>
-hipError_t launch_qb(const FwdParams& p) {
-    using S = FwdShape<D, QB>;
-    const int ntq = (p.max_nq + S::BQ - 1) / S::BQ;
+template <class T, int D>
+hipError_t launch(const FwdParams& p) {
+    constexpr int QB = ATTN_FWD_QB, BQ = kWaves * 32 * QB;
+    const int ntq = (p.max_nq + BQ - 1) / BQ;
     const int64_t nseq = (int64_t)p.L.B * p.L.H;
     const int64_t blocks = nseq * ntq;
     if (blocks == 0) return hipSuccess;
@@ -293,7 +420,7 @@ hipError_t launch_qb(const FwdParams& p) {
 
 template <class T>
 hipError_t launch_d(const FwdParams& p) {
-    return p.d == 64 ? launch_qb<T, 64, ATTN_FWD_QB>(p) : launch_qb<T, 128, ATTN_FWD_QB>(p);
+    return p.d == 64 ? launch<T, 64>(p) : launch<T, 128>(p);
 }
 
 }  // namespace
