@@ -90,7 +90,8 @@ __device__ inline void store_staged(uint16_t* __restrict__ dst, const uint16_t* 
 }
 
 // ============================================================================
-// dQ and D: one work group per (batch*head, 128 query rows), 4 waves x 32 rows.
+// dQ and D: one work group per (sequence, 128 query rows), 4 waves x 32 rows.
+// K and V tiles of 64 keys stream through LDS by DMA (double-buffered).
 // ============================================================================
 constexpr int kQ_BQ = 128;
 constexpr int kQ_BK = 64;
@@ -102,15 +103,17 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                         const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
                         float* __restrict__ Delta, uint16_t* __restrict__ dQ, SeqLayout L, int ntq,
                         float scale, float c) {
-    constexpr int STR = LdsStride<D>::value;
+    using DT = DmaTile<D, kQ_BK>;
+    constexpr int STR = LdsStride<D>::value;  // row stride of the output staging
     constexpr int KS = D / 16, DB = D / 32, KB = kQ_BK / 32;
-    constexpr int TILE = kQ_BK * STR;
-    static_assert(kQ_BQ * STR <= 2 * TILE, "staging must fit in the K buffers");
-    using Copy = TileCopy<kQ_BK, D, kThreads>;
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[2 * TILE];
+    constexpr int TB = DT::ELEMS;
+    constexpr int SMEM = (kQ_BQ * STR > 4 * TB) ? kQ_BQ * STR : 4 * TB;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM];
+    uint16_t* const Ks = smem;           // K tiles: buffers 0, 1
+    uint16_t* const Vs = smem + 2 * TB;  // V tiles: buffers 0, 1
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n32 = lane & 31, h = lane >> 5;
     const int item = xcd_contiguous(blockIdx.x, gridDim.x);
     const Seq sq = resolve(L, item / ntq);
@@ -146,14 +149,14 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     const int qlast = min(q0 + kQ_BQ, nq) - 1;
     const TileRange tr = tile_range(sq.key_lo(q0), sq.key_hi(qlast), sq.key_lo(qlast),
                                     min(sq.key_hi(q0), nk - 1), nk, kQ_BK);
-    Copy kc(tid), vc(tid);
+    const uint32_t goff = DT::lane_goff(lane);
     if (tr.end > tr.first) {
-        const int b0 = (tr.first & 1) * TILE;
-        kc.load(Kh, tr.first * kQ_BK, nk, tid);
-        vc.load(Vh, tr.first * kQ_BK, nk, tid);
-        kc.store(Ks + b0);
-        vc.store(Vs + b0);
+        dma_tile<D, kQ_BK>(Kh, tr.first * kQ_BK, nk, Ks + (tr.first & 1) * TB, w, lane, goff);
+        dma_tile<D, kQ_BK>(Vh, tr.first * kQ_BK, nk, Vs + (tr.first & 1) * TB, w, lane, goff);
     }
+    // Unconditional: the fragments above and the first tiles have landed (the
+    // compiler counts only its own loads; see the forward kernel).
+    wait_dma();
     __syncthreads();
 
     f32x16 dqacc[DB];
@@ -161,18 +164,21 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) dqacc[db][e] = 0.f;
-    const int tr_off = tr_lane_offset<STR>(lane);
+    const uint32_t fo[2] = {DT::frag_lane(lane, 0), DT::frag_lane(lane, 1)};
+    const uint32_t to0 = DT::tr_lane(lane, 0), to1 = DT::tr_lane(lane, 1);
 
-    auto step = [&](int jt, auto masked_tag) {
+    auto step = [&](int jt, auto masked_tag) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_tag)::value;
-        const int buf = (jt & 1) * TILE;
+        const int buf = jt & 1;
         const int k0 = jt * kQ_BK;
-        const bool more = jt + 1 < tr.end;
-        if (more) {
-            kc.load(Kh, k0 + kQ_BK, nk, tid);
-            vc.load(Vh, k0 + kQ_BK, nk, tid);
+        // the other buffers held tile jt-1, which every wave has finished
+        if (jt + 1 < tr.end) {
+            dma_tile<D, kQ_BK>(Kh, k0 + kQ_BK, nk, Ks + (1 - buf) * TB, w, lane, goff);
+            dma_tile<D, kQ_BK>(Vh, k0 + kQ_BK, nk, Vs + (1 - buf) * TB, w, lane, goff);
         }
         if (!MASKED || (wq0 < nq && k0 <= sq.key_hi(wq0 + 31) && k0 + kQ_BK - 1 >= sq.key_lo(wq0))) {
+            const char* kt = (const char*)(Ks + buf * TB);
+            const char* vt = (const char*)(Vs + buf * TB);
             // ---- S^T = K Q^T and dP^T = V dO^T
             f32x16 s[KB], dp[KB];
             prio_mfma();
@@ -183,11 +189,11 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                     s[kb][e] = 0.f;
                     dp[kb][e] = 0.f;
                 }
-                const int roff = buf + (kb * 32 + n32) * STR + 8 * h;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    s[kb] = mfma32<T>(*(const u32x4*)(Ks + roff + 16 * ks), qf[ks], s[kb]);
-                    dp[kb] = mfma32<T>(*(const u32x4*)(Vs + roff + 16 * ks), dof[ks], dp[kb]);
+                    const int o = DT::frag_blk(kb, ks);
+                    s[kb] = mfma32<T>(*(const u32x4*)(kt + fo[ks & 1] + o), qf[ks], s[kb]);
+                    dp[kb] = mfma32<T>(*(const u32x4*)(vt + fo[ks & 1] + o), dof[ks], dp[kb]);
                 }
             }
             sched_reads_ahead<4, 2 * KB * KS, 1>();
@@ -209,8 +215,7 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                 }
                 pack_acc_as_b<T>(ds, b[kb][0], b[kb][1]);
             }
-            // ---- dQ^T += K^T dS^T
-            const uint16_t* kt = Ks + buf + tr_off;
+            // ---- dQ^T += K^T dS^T (K^T read transposed from the K tile)
             prio_mfma();
 #pragma unroll
             for (int db = 0; db < DB; ++db)
@@ -218,27 +223,26 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                 for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                     for (int t = 0; t < 2; ++t)
-                        dqacc[db] = mfma32<T>(tr_operand<STR>(kt, kb * 32 + 16 * t, 32 * db), b[kb][t], dqacc[db]);
+                        dqacc[db] = mfma32<T>(tr_operand_dma(kt, to0, to1, DT::tr_blk(2 * kb + t, db)), b[kb][t],
+                                              dqacc[db]);
             sched_reads_ahead<8, DB * KB * 2, 2>();
             prio_normal();
         }
-        if (more) {
-            kc.store(Ks + TILE - buf);
-            vc.store(Vs + TILE - buf);
-        }
+        wait_dma();
         __syncthreads();
     };
     for (int jt = tr.first; jt < tr.full_first; ++jt) step(jt, Flag<true>{});
     for (int jt = tr.full_first; jt < tr.full_end; ++jt) step(jt, Flag<false>{});
     for (int jt = tr.full_end; jt < tr.end; ++jt) step(jt, Flag<true>{});
 
-    stage_transposed<T, D, STR>(Ks, 32 * w + n32, h, dqacc, scale);
+    stage_transposed<T, D, STR>(smem, 32 * w + n32, h, dqacc, scale);
     __syncthreads();
-    store_staged<D, STR>(dQ + sq.qrow0 * D, Ks, kQ_BQ, q0, nq, tid);
+    store_staged<D, STR>(dQ + sq.qrow0 * D, smem, kQ_BQ, q0, nq, tid);
 }
 
 // ============================================================================
-// dK and dV: one work group per (batch*head, 128 key rows), 4 waves x 32 keys.
+// dK and dV: one work group per (sequence, 128 key rows), 4 waves x 32 keys.
+// Q and dO tiles of 64 rows stream through LDS by DMA (double-buffered).
 // At d = 128 the resident K, V fragments and both accumulators need more than
 // the 256 registers of a two-waves-per-SIMD budget, so this kernel runs one
 // wave per SIMD there (forcing two spills heavily); at d = 64 it runs two.
@@ -253,16 +257,18 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
                           const float* __restrict__ LSE, const float* __restrict__ Delta,
                           uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, SeqLayout L, int ntk,
                           float scale, float c) {
-    constexpr int STR = LdsStride<D>::value;
+    using DT = DmaTile<D, kK_BQ>;
+    constexpr int STR = LdsStride<D>::value;  // row stride of the output staging
     constexpr int KS = D / 16, DB = D / 32, QB = kK_BQ / 32;
-    constexpr int TILE = kK_BQ * STR;
-    static_assert(kK_BK * STR <= 2 * TILE, "staging must fit in the Q buffers");
-    using Copy = TileCopy<kK_BQ, D, kThreads>;
-    __shared__ __attribute__((aligned(16))) uint16_t Qs[2 * TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t dOs[2 * TILE];
+    constexpr int TB = DT::ELEMS;
+    constexpr int SMEM = (kK_BK * STR > 4 * TB) ? kK_BK * STR : 4 * TB;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM];
     __shared__ __attribute__((aligned(16))) float stats[2][2][kK_BQ];  // [buffer][lse*log2e, D][row]
+    uint16_t* const Qs = smem;            // Q tiles: buffers 0, 1
+    uint16_t* const dOs = smem + 2 * TB;  // dO tiles: buffers 0, 1
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n32 = lane & 31, h = lane >> 5;
     const int item = xcd_contiguous(blockIdx.x, gridDim.x);
     const Seq sq = resolve(L, item / ntk);
@@ -293,7 +299,7 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     // their lse is +inf, so P = 0).
     const int klast = min(k0 + kK_BK, nk) - 1;
     const TileRange tr = tile_range(sq.row_lo(k0), sq.row_hi(klast), sq.row_lo(klast), sq.row_hi(k0), nq, kK_BQ);
-    Copy qc(tid), oc(tid);
+    const uint32_t goff = DT::lane_goff(lane);
     float st_l = kPosInf, st_d = 0.f;
     auto load_stats = [&](int r0) {
         if (tid < kK_BQ) {
@@ -310,13 +316,12 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     };
     if (tr.end > tr.first) {
         const int r0 = tr.first * kK_BQ, sb0 = tr.first & 1;
-        qc.load(Qh, r0, nq, tid);
-        oc.load(dOh, r0, nq, tid);
+        dma_tile<D, kK_BQ>(Qh, r0, nq, Qs + sb0 * TB, w, lane, goff);
+        dma_tile<D, kK_BQ>(dOh, r0, nq, dOs + sb0 * TB, w, lane, goff);
         load_stats(r0);
-        qc.store(Qs + sb0 * TILE);
-        oc.store(dOs + sb0 * TILE);
         store_stats(sb0);
     }
+    wait_dma();  // unconditional (see the dq kernel)
     __syncthreads();
 
     f32x16 dkacc[DB], dvacc[DB];
@@ -327,19 +332,22 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
             dkacc[db][e] = 0.f;
             dvacc[db][e] = 0.f;
         }
-    const int tr_off = tr_lane_offset<STR>(lane);
+    const uint32_t fo[2] = {DT::frag_lane(lane, 0), DT::frag_lane(lane, 1)};
+    const uint32_t to0 = DT::tr_lane(lane, 0), to1 = DT::tr_lane(lane, 1);
 
-    auto step = [&](int it, auto masked_tag) {
+    auto step = [&](int it, auto masked_tag) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_tag)::value;
         const int sb = it & 1;
-        const int buf = sb * TILE;
         const int qq0 = it * kK_BQ;
         const bool more = it + 1 < tr.end;
+        // the other buffers held tile it-1, which every wave has finished
         if (more) {
-            qc.load(Qh, qq0 + kK_BQ, nq, tid);
-            oc.load(dOh, qq0 + kK_BQ, nq, tid);
+            dma_tile<D, kK_BQ>(Qh, qq0 + kK_BQ, nq, Qs + (1 - sb) * TB, w, lane, goff);
+            dma_tile<D, kK_BQ>(dOh, qq0 + kK_BQ, nq, dOs + (1 - sb) * TB, w, lane, goff);
             load_stats(qq0 + kK_BQ);
         }
+        const char* qt_ = (const char*)(Qs + sb * TB);
+        const char* ot_ = (const char*)(dOs + sb * TB);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const int qb0 = qq0 + 32 * qb;  // first query row of this 32-row block
@@ -352,12 +360,12 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
                 s[e] = 0.f;
                 dp[e] = 0.f;
             }
-            const int roff = buf + (32 * qb + n32) * STR + 8 * h;
             prio_mfma();
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                s = mfma32<T>(*(const u32x4*)(Qs + roff + 16 * ks), kf[ks], s);
-                dp = mfma32<T>(*(const u32x4*)(dOs + roff + 16 * ks), vf[ks], dp);
+                const int o = DT::frag_blk(qb, ks);
+                s = mfma32<T>(*(const u32x4*)(qt_ + fo[ks & 1] + o), kf[ks], s);
+                dp = mfma32<T>(*(const u32x4*)(ot_ + fo[ks & 1] + o), vf[ks], dp);
             }
             sched_reads_ahead<4, 2 * KS, 1>();
             prio_normal();
@@ -387,36 +395,35 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
             u32x4 bp[2], bds[2];
             pack_acc_as_b<T>(p, bp[0], bp[1]);
             pack_acc_as_b<T>(ds, bds[0], bds[1]);
-            // ---- dV^T += dO^T P and dK^T += Q^T dS
+            // ---- dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T read transposed)
             prio_mfma();
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    dvacc[db] = mfma32<T>(tr_operand<STR>(dOs + buf + tr_off, 32 * qb + 16 * t, 32 * db), bp[t], dvacc[db]);
-                    dkacc[db] = mfma32<T>(tr_operand<STR>(Qs + buf + tr_off, 32 * qb + 16 * t, 32 * db), bds[t], dkacc[db]);
+                    const int o = DT::tr_blk(2 * qb + t, db);
+                    dvacc[db] = mfma32<T>(tr_operand_dma(ot_, to0, to1, o), bp[t], dvacc[db]);
+                    dkacc[db] = mfma32<T>(tr_operand_dma(qt_, to0, to1, o), bds[t], dkacc[db]);
                 }
             sched_reads_ahead<8, DB * 4, 2>();
             prio_normal();
         }
-        if (more) {
-            qc.store(Qs + TILE - buf);
-            oc.store(dOs + TILE - buf);
-            store_stats(sb ^ 1);
-        }
+        // stats[sb ^ 1] held tile it-1's statistics, which every wave has finished
+        if (more) store_stats(sb ^ 1);
+        wait_dma();
         __syncthreads();
     };
     for (int it = tr.first; it < tr.full_first; ++it) step(it, Flag<true>{});
     for (int it = tr.full_first; it < tr.full_end; ++it) step(it, Flag<false>{});
     for (int it = tr.full_end; it < tr.end; ++it) step(it, Flag<true>{});
 
-    stage_transposed<T, D, STR>(Qs, 32 * w + n32, h, dkacc, scale);
+    stage_transposed<T, D, STR>(smem, 32 * w + n32, h, dkacc, scale);
     __syncthreads();
-    store_staged<D, STR>(dK + sq.krow0 * D, Qs, kK_BK, k0, nk, tid);
+    store_staged<D, STR>(dK + sq.krow0 * D, smem, kK_BK, k0, nk, tid);
     __syncthreads();
-    stage_transposed<T, D, STR>(Qs, 32 * w + n32, h, dvacc, 1.f);
+    stage_transposed<T, D, STR>(smem, 32 * w + n32, h, dvacc, 1.f);
     __syncthreads();
-    store_staged<D, STR>(dV + sq.krow0 * D, Qs, kK_BK, k0, nk, tid);
+    store_staged<D, STR>(dV + sq.krow0 * D, smem, kK_BK, k0, nk, tid);
 }
 
 template <class T, int D>

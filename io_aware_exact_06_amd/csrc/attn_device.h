@@ -127,58 +127,123 @@ struct LdsStride<64> {
     static constexpr int value = 72;
 };
 
-// Copy a tile of ROWS x D 16-bit values (rows r0 .. r0+ROWS-1 of a row-major
-// [nrows, D] array, nrows >= 1) from global memory into registers, 16 bytes
-// per chunk, then into an LDS tile of row stride LdsStride<D>.
+// ---------------------------------------------------------------------------
+// Tiles loaded by DMA (global_load_lds_dwordx4: global memory straight into
+// LDS, no registers).
 //
-// Each thread's chunk offsets inside a tile are computed once and stay in
-// registers for the whole loop; the tile's base address is wave-uniform.  A
-// load is then one instruction on an SGPR base plus a fixed VGPR offset, and
-// no address register is ever recycled while a prefetch is still in flight
-// (recycling one makes the compiler wait for that prefetch before the next
-// use of the register).  Rows at or beyond nrows read row nrows-1 instead, so
-// every load stays in bounds without exec-mask branches; callers mask or
-// discard the duplicated rows.  THREADS threads split the tile.
-template <int ROWS, int D, int THREADS>
-struct TileCopy {
-    static constexpr int CH = D / 8;                      // 16-byte chunks per row
-    static constexpr int CPT = ROWS * CH / THREADS;       // chunks per thread
-    static_assert(ROWS * CH % THREADS == 0, "tile must split evenly over the threads");
-    static constexpr int STR = LdsStride<D>::value;
+// LDS image of a ROWS x D tile of 16-bit values: the tile is cut into blocks
+// of 16 rows x 4 chunks (a chunk is 8 values, 16 bytes); block (rg, cg) sits at
+// byte (rg * CG + cg) * 1024, CG = D / 32.  Inside a block, row r takes 64
+// bytes at r * 64 and its chunk c is stored in slot c ^ ((r >> 2) & 3).  One
+// wave-wide DMA instruction fills one block (lane L writes bytes 16 L ..
+// 16 L + 15, i.e. row L / 4, slot L % 4), so every global read is 16 rows x 64
+// contiguous bytes.  The slot swizzle makes both LDS read patterns of the
+// kernels conflict-free: 16 lanes reading one chunk of 16 consecutive rows
+// (128-bit reads of MFMA row fragments) and 16 lanes reading 4 rows x 32 bytes
+// (transpose reads) each touch 16 distinct bank groups.
+template <int D, int ROWS>
+struct DmaTile {
+    static constexpr int CG = D / 32;                 // chunk groups per row
+    static constexpr int BYTES = ROWS * D * 2;        // one tile
+    static constexpr int ELEMS = ROWS * D;
+    static constexpr int NBLK = (ROWS / 16) * CG;     // 1 KB blocks per tile
+    static constexpr int PER_WAVE = NBLK / 4;         // DMA instructions per wave (4 waves)
+    static_assert(NBLK % 4 == 0, "tile blocks must split over four waves");
 
-    u32x4 r[CPT];
-    uint32_t goff[CPT];  // byte offset of chunk i inside a global tile
-    uint32_t loff[CPT];  // element offset of chunk i inside an LDS tile
-
-    __device__ inline explicit TileCopy(int tid) {
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int c = tid + i * THREADS;
-            goff[i] = (uint32_t)((c / CH) * D + 8 * (c % CH)) * 2u;
-            loff[i] = (uint32_t)((c / CH) * STR + 8 * (c % CH));
-        }
+    // Byte offset, inside the global tile, of the chunk this lane loads for
+    // a block (excluding the block's base).
+    __device__ static inline uint32_t lane_goff(int lane) {
+        const int r = lane >> 2, c = (lane & 3) ^ ((r >> 2) & 3);
+        return (uint32_t)(r * D + c * 8) * 2u;
     }
 
-    __device__ inline void load(const uint16_t* __restrict__ src, int r0, int nrows, int tid) {
-        const char* base = (const char*)(src + (int64_t)r0 * D);
-        if (r0 + ROWS <= nrows) {
-#pragma unroll
-            for (int i = 0; i < CPT; ++i) r[i] = *(const u32x4*)(base + goff[i]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < CPT; ++i) {
-                const int c = tid + i * THREADS;
-                const int row = min(c / CH, nrows - 1 - r0);
-                r[i] = *(const u32x4*)(base + (uint32_t)(row * D + 8 * (c % CH)) * 2u);
-            }
-        }
+    // 128-bit read of an MFMA row fragment: row 32 rb + n32 (n32 = lane % 32),
+    // chunk 2 ks + lane / 32.  frag_lane(lane, ks & 1) + frag_blk(rb, ks)
+    // (bytes; the lane part is loop-invariant, the block part a constant).
+    __device__ static inline uint32_t frag_lane(int lane, int p) {
+        const int n32 = lane & 31, h = lane >> 5, r = n32 & 15;
+        return (uint32_t)((n32 >> 4) * CG * 1024 + r * 64 + (((2 * p + h) ^ ((r >> 2) & 3)) << 4));
     }
+    static constexpr int frag_blk(int rb, int ks) { return (2 * rb * CG + ks / 2) * 1024; }
 
-    __device__ inline void store(uint16_t* dst) const {
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) *(u32x4*)(dst + loff[i]) = r[i];
+    // Transpose read e (e = 0, 1) yielding half of the A operand
+    // A[m][k] = T[16 rs + k][32 db + m] of a 32x32x16 MFMA (see lds_read_tr):
+    // tr_lane(lane, e) + tr_blk(rs, db).
+    __device__ static inline uint32_t tr_lane(int lane, int e) {
+        const int h = lane >> 5, g16 = lane & 15, x = (lane >> 4) & 1;
+        const int row = 8 * e + 4 * h + (g16 >> 2);
+        const int cc = 2 * x + ((g16 & 3) >> 1);
+        return (uint32_t)(row * 64 + ((cc ^ (2 * e + h)) << 4) + (g16 & 1) * 8);
     }
+    static constexpr int tr_blk(int rs, int db) { return (rs * CG + db) * 1024; }
 };
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ inline uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One DMA instruction: 16 bytes per lane from base + voff (global) into LDS at
+// lds_byte + 16 * lane.  Issued in assembly: the compiler does not track it,
+// so it neither waits for it before unrelated LDS reads nor reuses LDS values
+// across it ("memory" clobber); kernels wait with wait_dma() and a barrier
+// before any wave reads the tile.  M0 carries the LDS address and needs one
+// wait state after being written.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ inline void dma16(const void* base, uint32_t voff, uint32_t lds_byte) {
+    // base and lds_byte are wave-uniform; make that explicit for the SGPR operands
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const uint64_t sb = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b) |
+                        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32);
+    const void* sbase = (const void*)(uintptr_t)sb;
+    const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane(lds_byte);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// vmcnt(0): every DMA (and global load) of this wave has landed; expcnt and
+// lgkmcnt are not waited on.
+__device__ inline void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+// Issue the DMA of rows r0 .. r0+ROWS-1 of a [nrows, D] array into an LDS
+// tile (four waves share the work; w is the wave-uniform wave index).  Rows
+// at or beyond nrows read row nrows-1 (callers mask or discard them).
+template <int D, int ROWS>
+__device__ inline void dma_tile(const uint16_t* __restrict__ src, int r0, int nrows, const uint16_t* lds_tile,
+                                int w, int lane, uint32_t goff) {
+    using DT = DmaTile<D, ROWS>;
+    const char* base = (const char*)(src + (int64_t)r0 * D);
+    const uint32_t lt = lds_addr(lds_tile);
+    if (r0 + ROWS <= nrows) {
+#pragma unroll
+        for (int i = 0; i < DT::PER_WAVE; ++i) {
+            const int b = w + 4 * i, rg = b / DT::CG, cg = b % DT::CG;
+            dma16(base + (rg * 16 * D + cg * 32) * 2, goff, lt + b * 1024);
+        }
+    } else {
+        const int r = lane >> 2, c = (lane & 3) ^ ((r >> 2) & 3);
+#pragma unroll
+        for (int i = 0; i < DT::PER_WAVE; ++i) {
+            const int b = w + 4 * i, rg = b / DT::CG, cg = b % DT::CG;
+            const int row = min(rg * 16 + r, nrows - 1 - r0);
+            dma16(base, (uint32_t)(row * D + cg * 32 + c * 8) * 2u, lt + b * 1024);
+        }
+    }
+}
+
+// A operand of a 32x32x16 MFMA read transposed from a DMA tile (two transpose
+// reads; tile_at is the tile's byte address, ofs0/ofs1 the tr_lane offsets).
+__device__ inline u32x4 tr_operand_dma(const char* tile, uint32_t ofs0, uint32_t ofs1, int blk) {
+    const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + ofs0 + blk)));
+    const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + ofs1 + blk)));
+    const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+    return a;
+}
 
 // Offset (in elements, relative to the start of a 32-column block of a 16-row
 // step) of this lane's address for the transpose read that yields the A

@@ -55,95 +55,13 @@ constexpr int kBK = 64;        // key rows per tile
 #endif
 constexpr float kLazy = 8.0f;  // rescale only when the maximum grows by more than 2^8
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// LDS image of a 64 x D tile written by the DMA path.  The tile is cut into
-// blocks of 16 rows x 4 chunks (a chunk is 8 values, 16 bytes); block
-// (rg, cg) sits at byte (rg * CG + cg) * 1024, CG = D / 32.  Inside a block,
-// row r takes 64 bytes at r * 64 and its chunk c is stored in slot
-// c ^ ((r >> 2) & 3).  One wave-wide DMA instruction fills one block (lane L
-// writes bytes 16 L .. 16 L + 15, i.e. row L / 4, slot L % 4), so every
-// global read is 16 rows x 64 contiguous bytes.  The slot swizzle makes both
-// LDS read patterns conflict-free: 16 lanes reading one chunk of 16
-// consecutive rows (128-bit reads) and 16 lanes reading 4 rows x 32 bytes
-// (transpose reads) each touch 16 distinct bank groups.
-template <int D>
-struct DmaTile {
-    static constexpr int CG = D / 32;          // chunk groups per row
-    static constexpr int BYTES = kBK * D * 2;  // one tile
-    static constexpr int PER_WAVE = CG;        // blocks (DMA instructions) per wave per tile
-
-    // Byte offset, inside this lane's global tile, of the chunk it loads for
-    // the block of chunk group cg of row group rg (excluding the block's base).
-    __device__ static inline uint32_t lane_goff(int lane) {
-        const int r = lane >> 2, c = (lane & 3) ^ ((r >> 2) & 3);
-        return (uint32_t)(r * D + c * 8) * 2u;
-    }
-    // Block b of a tile handled by wave w in its i-th instruction.
-    __device__ static inline int block(int w, int i) { return w + kWaves * i; }
-};
-
-// One DMA instruction: 16 bytes per lane from sbase + voff (global) into LDS
-// at lds + 16 * lane.  Issued in assembly: the compiler does not track it,
-// so it neither waits for it before unrelated LDS reads nor reuses LDS
-// values across it ("memory" clobber); the kernel waits for completion with
-// wait_dma() and a barrier before any wave reads the tile.  M0 carries the
-// LDS address and needs one wait state after being written.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ inline void dma16(const void* base, uint32_t voff, uint32_t lds_byte) {
-    // base and lds_byte are wave-uniform; make that explicit for the SGPR operands
-    const uint64_t b = (uint64_t)(uintptr_t)base;
-    const uint64_t sb = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b) |
-                        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32);
-    const void* sbase = (const void*)(uintptr_t)sb;
-    const uint32_t lds = (uint32_t)__builtin_amdgcn_readfirstlane(lds_byte);
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :
-                 : "v"(voff), "s"(sbase), "s"(lds)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-__device__ inline uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// Issue the DMA of key/value rows r0 .. r0+63 of a [nrows, D] array into an
-// LDS tile.  Rows at or beyond nrows read row nrows-1 (callers mask them).
-// w is the (wave-uniform) wave index.
-template <int D>
-__device__ inline void dma_tile(const uint16_t* __restrict__ src, int r0, int nrows, const uint16_t* lds_tile, int w,
-                                int lane, uint32_t goff) {
-    using DT = DmaTile<D>;
-    const char* base = (const char*)(src + (int64_t)r0 * D);
-    const uint32_t lt = lds_addr(lds_tile);
-    if (r0 + kBK <= nrows) {
-#pragma unroll
-        for (int i = 0; i < DT::PER_WAVE; ++i) {
-            const int b = DT::block(w, i), rg = b / DT::CG, cg = b % DT::CG;
-            dma16(base + (rg * 16 * D + cg * 32) * 2, goff, lt + b * 1024);
-        }
-    } else {
-        const int r = lane >> 2, c = (lane & 3) ^ ((r >> 2) & 3);
-#pragma unroll
-        for (int i = 0; i < DT::PER_WAVE; ++i) {
-            const int b = DT::block(w, i), rg = b / DT::CG, cg = b % DT::CG;
-            const int row = min(rg * 16 + r, nrows - 1 - r0);
-            dma16(base, (uint32_t)(row * D + cg * 32 + c * 8) * 2u, lt + b * 1024);
-        }
-    }
-}
-
-__device__ inline void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0); expcnt, lgkmcnt not waited on
-
 template <class T, int D, int QB>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(QB == 1 ? 2 : 1, QB == 1 ? 2 : 1)))
 void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                      float* __restrict__ LSE, SeqLayout L, int ntq, float scale, float c) {
-    using DT = DmaTile<D>;
+    using DT = DmaTile<D, kBK>;
     constexpr int KS = D / 16;                 // MFMA k-steps of S^T over d
     constexpr int DB = D / 32;                 // 32-row blocks of O^T
     constexpr int TB = DT::BYTES / 2;          // tile size in 16-bit elements
@@ -183,25 +101,10 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     const TileRange tr = tile_range(sq.key_lo(q0), sq.key_hi(qlast), sq.key_lo(qlast),
                                     min(sq.key_hi(q0), nk - 1), nk, kBK);
 
-    // Per-lane LDS read offsets (bytes, relative to a tile):
-    //  K fragment of k-step ks, key block kb: row kb*32 + n32, chunk 2 ks + h
-    //    -> kofs[ks & 1] + (2 kb * CG + ks / 2) * 1024 (the n32 / 16 row group folded in);
-    //  V^T transpose read e (rows 8 e + 4 h + g16 / 4 of a 16-row step), 32-column block db
-    //    -> vofs[e] + ((2 kb + t) * CG + db) * 1024.
-    uint32_t kofs[2], vofs[2];
-    {
-        const int r = n32 & 15, q = (r >> 2) & 3;
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-            kofs[p] = (uint32_t)((n32 >> 4) * DT::CG * 1024 + r * 64 + (((2 * p + h) ^ q) << 4));
-        const int g16 = lane & 15, x = (lane >> 4) & 1;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int row = 8 * e + 4 * h + (g16 >> 2);
-            const int cc = 2 * x + ((g16 & 3) >> 1);
-            vofs[e] = (uint32_t)(row * 64 + ((cc ^ (2 * e + h)) << 4) + (g16 & 1) * 8);
-        }
-    }
+    // Per-lane LDS read offsets (bytes, relative to a tile): K row fragments
+    // (128-bit reads) and V^T operands (transpose reads).
+    const uint32_t kofs[2] = {DT::frag_lane(lane, 0), DT::frag_lane(lane, 1)};
+    const uint32_t vofs0 = DT::tr_lane(lane, 0), vofs1 = DT::tr_lane(lane, 1);
     const uint32_t goff = DT::lane_goff(lane);
 
     f32x16 oacc[QB][DB];
@@ -234,7 +137,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const u32x4 a = *(const u32x4*)(kt + kofs[ks & 1] + (2 * kb * DT::CG + ks / 2) * 1024);
+                const u32x4 a = *(const u32x4*)(kt + kofs[ks & 1] + DT::frag_blk(kb, ks));
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) sacc[PAR][qb][kb] = mfma32<T>(a, qf[qb][ks], sacc[PAR][qb][kb]);
             }
@@ -242,10 +145,10 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 
     // Prologue: tiles first (K, V) and first+1 (K) in flight, then the scores of the first.
     if (tr.end > tr.first) {
-        dma_tile<D>(Kh, tr.first * kBK, nk, Kb + (tr.first & 1) * TB, w, lane, goff);
-        dma_tile<D>(Vh, tr.first * kBK, nk, Vb + (tr.first & 1) * TB, w, lane, goff);
+        dma_tile<D, kBK>(Kh, tr.first * kBK, nk, Kb + (tr.first & 1) * TB, w, lane, goff);
+        dma_tile<D, kBK>(Vh, tr.first * kBK, nk, Vb + (tr.first & 1) * TB, w, lane, goff);
         if (tr.first + 1 < tr.end)
-            dma_tile<D>(Kh, (tr.first + 1) * kBK, nk, Kb + ((tr.first + 1) & 1) * TB, w, lane, goff);
+            dma_tile<D, kBK>(Kh, (tr.first + 1) * kBK, nk, Kb + ((tr.first + 1) & 1) * TB, w, lane, goff);
     }
     // Unconditional: the Q fragments and the first tiles have landed.  The
     // compiler counts only its own loads in vmcnt; waiting for everything
@@ -270,8 +173,8 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         // are free) and the DMA of K(jt+1), V(jt) has landed.
         __syncthreads();
         if (NEXT) {
-            if (jt + 2 < tr.end) dma_tile<D>(Kh, k0 + 2 * kBK, nk, Kb + PAR * TB, w, lane, goff);
-            dma_tile<D>(Vh, k0 + kBK, nk, Vb + (1 - PAR) * TB, w, lane, goff);
+            if (jt + 2 < tr.end) dma_tile<D, kBK>(Kh, k0 + 2 * kBK, nk, Kb + PAR * TB, w, lane, goff);
+            dma_tile<D, kBK>(Vh, k0 + kBK, nk, Vb + (1 - PAR) * TB, w, lane, goff);
         }
         float mc[QB];
 #pragma unroll
@@ -335,12 +238,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    const int blk = ((2 * kb + t) * DT::CG + db) * 1024;
-                    const u32x2 lo = __builtin_bit_cast(
-                        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + vofs[0] + blk)));
-                    const u32x2 hi = __builtin_bit_cast(
-                        u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + vofs[1] + blk)));
-                    const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+                    const u32x4 a = tr_operand_dma(vt, vofs0, vofs1, DT::tr_blk(2 * kb + t, db));
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32<T>(a, pf[qb][kb][t], oacc[qb][db]);
                 }
