@@ -24,7 +24,9 @@ _lib = None
 
 _P = ctypes.POINTER(ctypes.c_double)
 _PI = ctypes.POINTER(ctypes.c_int64)
+_PB = ctypes.POINTER(ctypes.c_uint8)
 _I = ctypes.c_int64
+_BM = [_PB, _I, _I, _I, _I]  # block mask, bq, bk, nqb, nkb
 
 
 GCC_FLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-shared", "-fPIC"]
@@ -50,13 +52,13 @@ class OracleLib:
 
     def __init__(self, path: str):
         lib = ctypes.CDLL(path)
-        lib.oracle_attn_fwd.argtypes = [_I, _I, _I, _I, _P, _P, _P, _PI, ctypes.c_int, _I, _I,
+        lib.oracle_attn_fwd.argtypes = [_I, _I, _I, _I, _P, _P, _P, _PI, ctypes.c_int, _I, _I, *_BM,
                                         ctypes.c_double, _P, _P]
         lib.oracle_attn_fwd.restype = ctypes.c_int
-        lib.oracle_attn_fwd_online.argtypes = [_I, _I, _I, _I, _P, _P, _P, _PI, ctypes.c_int, _I, _I,
+        lib.oracle_attn_fwd_online.argtypes = [_I, _I, _I, _I, _P, _P, _P, _PI, ctypes.c_int, _I, _I, *_BM,
                                                ctypes.c_double, _I, _P, _P]
         lib.oracle_attn_fwd_online.restype = ctypes.c_int
-        lib.oracle_attn_bwd.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _PI, ctypes.c_int, _I, _I,
+        lib.oracle_attn_bwd.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _PI, ctypes.c_int, _I, _I, *_BM,
                                         ctypes.c_double, _PI, _I, _P, _PI, _I, _P, _P]
         lib.oracle_attn_bwd.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
@@ -67,13 +69,16 @@ class OracleLib:
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())
 
-    def fwd(self, q, k, v, causal: bool, scale: float, qpos=None, window=(-1, -1)):
+    def fwd(self, q, k, v, causal: bool, scale: float, qpos=None, window=(-1, -1), block_mask=None,
+            block=(128, 128)):
         """Three-pass forward.  Returns (o [G,nq,d], lse [G,nq]).
 
         qpos gives the key position of each query row (default i + nk - nq:
         rows aligned to the end of the keys, the identity when nq == nk).  Key
         j is visible to row i iff (not causal or j <= qpos[i]) and, for a
-        window (wl, wr) with -1 meaning unbounded, qpos[i] - wl <= j <= qpos[i] + wr.
+        window (wl, wr) with -1 meaning unbounded, qpos[i] - wl <= j <= qpos[i] + wr,
+        and, for a block mask ([nqb, nkb] shared by all heads or [G, nqb, nkb],
+        block = (bq, bk)), block_mask[qpos[i] // bq, j // bk] != 0.
         """
         q, k, v = _f64(q), _f64(k), _f64(v)
         G, nq, d = q.shape
@@ -83,14 +88,16 @@ class OracleLib:
         qpos = _qpos(qpos, nq, nk)
         o = np.empty((G, nq, d), np.float64)
         lse = np.empty((G, nq), np.float64)
+        bm = _block_mask(block_mask, block, G, qpos, nk)
         rc = self.lib.oracle_attn_fwd(G, nq, nk, d, _ptr(q), _ptr(k), _ptr(v), _iptr(qpos),
-                                      int(bool(causal)), int(window[0]), int(window[1]), float(scale),
+                                      int(bool(causal)), int(window[0]), int(window[1]), *bm, float(scale),
                                       _ptr(o), _ptr(lse))
         if rc != 0:
             raise MemoryError("oracle_attn_fwd failed (%d)" % rc)
         return o, lse
 
-    def fwd_online(self, q, k, v, causal: bool, scale: float, block: int, qpos=None, window=(-1, -1)):
+    def fwd_online(self, q, k, v, causal: bool, scale: float, block: int, qpos=None, window=(-1, -1),
+                   block_mask=None, mask_block=(128, 128)):
         """Block-wise running-max forward (the validator).  Returns (o, lse)."""
         q, k, v = _f64(q), _f64(k), _f64(v)
         G, nq, d = q.shape
@@ -98,15 +105,16 @@ class OracleLib:
         qpos = _qpos(qpos, nq, nk)
         o = np.empty((G, nq, d), np.float64)
         lse = np.empty((G, nq), np.float64)
+        bm = _block_mask(block_mask, mask_block, G, qpos, nk)
         rc = self.lib.oracle_attn_fwd_online(G, nq, nk, d, _ptr(q), _ptr(k), _ptr(v), _iptr(qpos),
-                                             int(bool(causal)), int(window[0]), int(window[1]),
+                                             int(bool(causal)), int(window[0]), int(window[1]), *bm,
                                              float(scale), int(block), _ptr(o), _ptr(lse))
         if rc != 0:
             raise RuntimeError("oracle_attn_fwd_online failed (%d)" % rc)
         return o, lse
 
     def bwd(self, q, k, v, dout, causal: bool, scale: float, rows=None, keys=None, qpos=None,
-            window=(-1, -1)):
+            window=(-1, -1), block_mask=None, block=(128, 128)):
         """Analytic backward.  Returns (dq, dk, dv).
 
         q, dout: [G, nq, d]; k, v: [G, nk, d]; qpos and window as in fwd.
@@ -133,8 +141,9 @@ class OracleLib:
         pad = np.zeros(1, np.int64)  # a valid pointer for an empty selection
         rp = None if rows_a is None else (rows_a if nrows else pad)
         kp = None if keys_a is None else (keys_a if nkeys else pad)
+        bm = _block_mask(block_mask, block, G, qpos, nk)
         rc = self.lib.oracle_attn_bwd(G, nq, nk, d, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _iptr(qpos),
-                                      int(bool(causal)), int(window[0]), int(window[1]), float(scale),
+                                      int(bool(causal)), int(window[0]), int(window[1]), *bm, float(scale),
                                       _iptr(rp), nrows, _ptr(dq), _iptr(kp), nkeys, _ptr(dk), _ptr(dv))
         if rc != 0:
             raise MemoryError("oracle_attn_bwd failed (%d)" % rc)
@@ -149,6 +158,27 @@ def _qpos(qpos, nq, nk):
     if qpos.shape != (nq,):
         raise ValueError("qpos must have one entry per query row")
     return qpos
+
+
+def _block_mask(block_mask, block, G, qpos, nk):
+    """ctypes arguments (pointer, bq, bk, nqb, nkb) of an optional block mask.
+
+    The mask is kept alive by the returned pointer object's _keep attribute."""
+    if block_mask is None:
+        return (None, 1, 1, 1, 1)
+    bq, bk = int(block[0]), int(block[1])
+    bm = np.asarray(block_mask)
+    if bm.ndim == 2:
+        bm = np.broadcast_to(bm, (G,) + bm.shape)
+    bm = np.ascontiguousarray(bm != 0, dtype=np.uint8)
+    if bm.ndim != 3 or bm.shape[0] != G:
+        raise ValueError("block mask must be [nqb, nkb] or [G, nqb, nkb]")
+    nqb, nkb = bm.shape[1], bm.shape[2]
+    if bq < 1 or bk < 1 or nkb * bk < nk or (len(qpos) and nqb * bq <= int(np.max(qpos))):
+        raise ValueError("block mask does not cover every (row position, key)")
+    ptr = bm.ctypes.data_as(_PB)
+    ptr._keep = bm
+    return (ptr, bq, bk, nqb, nkb)
 
 
 def _load() -> OracleLib:
@@ -184,16 +214,18 @@ def num_threads() -> int:
     return _load().num_threads()
 
 
-def fwd(q, k, v, causal: bool, scale: float, qpos=None, window=(-1, -1)):
-    return _load().fwd(q, k, v, causal, scale, qpos, window)
+def fwd(q, k, v, causal: bool, scale: float, qpos=None, window=(-1, -1), block_mask=None, block=(128, 128)):
+    return _load().fwd(q, k, v, causal, scale, qpos, window, block_mask, block)
 
 
-def fwd_online(q, k, v, causal: bool, scale: float, block: int, qpos=None, window=(-1, -1)):
-    return _load().fwd_online(q, k, v, causal, scale, block, qpos, window)
+def fwd_online(q, k, v, causal: bool, scale: float, block: int, qpos=None, window=(-1, -1), block_mask=None,
+               mask_block=(128, 128)):
+    return _load().fwd_online(q, k, v, causal, scale, block, qpos, window, block_mask, mask_block)
 
 
-def bwd(q, k, v, dout, causal: bool, scale: float, rows=None, keys=None, qpos=None, window=(-1, -1)):
-    return _load().bwd(q, k, v, dout, causal, scale, rows, keys, qpos, window)
+def bwd(q, k, v, dout, causal: bool, scale: float, rows=None, keys=None, qpos=None, window=(-1, -1),
+        block_mask=None, block=(128, 128)):
+    return _load().bwd(q, k, v, dout, causal, scale, rows, keys, qpos, window, block_mask, block)
 
 
 fwd.__doc__ = OracleLib.fwd.__doc__

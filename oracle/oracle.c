@@ -42,9 +42,9 @@
  *       dQ = scale * dS K
  *       dK = scale * dS^T Q
  *
- * Masks: causal, and an optional sliding window, with query rows placed at
- * key positions qpos (see visible()); rectangular n_q != n_k shapes align the
- * rows to the end of the key sequence.  Variable-length batches are handled
+ * Masks: causal, an optional sliding window and an optional block mask, with
+ * query rows placed at key positions qpos (see visible()); rectangular
+ * n_q != n_k shapes align the rows to the end of the key sequence.  Variable-length batches are handled
  * by the Python wrapper, one sequence at a time.
  *
  * Layout: every array is a batch of G independent heads, row-major
@@ -77,31 +77,41 @@ static double dot(const double* a, const double* b, int64_t d) {
  *     and (wl < 0 or j >= pos - wl)         -- sliding window to the left
  *     and (wr < 0 or j <= pos + wr)         -- sliding window to the right
  * (a local window of the kind the yunthe article's hybrid local/global block
- * uses).  wl = wr = -1 means no window.
+ * uses).  wl = wr = -1 means no window.  With a block mask (the all-zero-block
+ * skipping of the snabindia page's chapter 1 and section 3.1, here as an
+ * explicit mask), head g additionally needs
+ *     bm[g][pos / bq][j / bk] != 0
+ * -- the (query block, key block) pair takes part; bm is [G, nqb, nkb] bytes,
+ * nqb * bq >= largest position + 1, nkb * bk >= n_k.  bm = NULL: no block mask.
  */
 typedef struct {
     int causal;
     int64_t wl, wr;
+    const uint8_t* bm;
+    int64_t bq, bk, nqb, nkb;
 } mask_t;
 
-static int visible(mask_t mk, int64_t j, int64_t pos) {
+static int visible(mask_t mk, int64_t g, int64_t j, int64_t pos) {
     if (mk.causal && j > pos) return 0;
     if (mk.wl >= 0 && j < pos - mk.wl) return 0;
     if (mk.wr >= 0 && j > pos + mk.wr) return 0;
+    if (mk.bm && !mk.bm[(g * mk.nqb + pos / mk.bq) * mk.nkb + j / mk.bk]) return 0;
     return 1;
 }
 
 /*
  * Forward, three passes per query row.
  *   q: [G, nq, d]   k, v: [G, nk, d]   qpos: [nq] sequence position of each query row
+ *   causal, wl, wr, bm, bq, bk, nqb, nkb: the mask (see visible())
  *   o: [G, nq, d]   lse: [G, nq]
  * Returns 0, or -1 if a work buffer cannot be allocated.
  */
 int oracle_attn_fwd(int64_t G, int64_t nq, int64_t nk, int64_t d,
                     const double* q, const double* k, const double* v,
-                    const int64_t* qpos, int causal, int64_t wl, int64_t wr, double scale,
+                    const int64_t* qpos, int causal, int64_t wl, int64_t wr,
+                    const uint8_t* bm, int64_t bq, int64_t bk, int64_t nqb, int64_t nkb, double scale,
                     double* o, double* lse) {
-    const mask_t mk = {causal, wl, wr};
+    const mask_t mk = {causal, wl, wr, bm, bq, bk, nqb, nkb};
     int failed = 0;
 #pragma omp parallel
     {
@@ -120,7 +130,7 @@ int oracle_attn_fwd(int64_t G, int64_t nq, int64_t nk, int64_t d,
             double* oi = o + (g * nq + i) * d;
             /* pass 1: scores */
             for (int64_t j = 0; j < nk; ++j)
-                s[j] = visible(mk, j, qpos[i]) ? scale * dot(qi, kg + j * d, d) : -INFINITY;
+                s[j] = visible(mk, g, j, qpos[i]) ? scale * dot(qi, kg + j * d, d) : -INFINITY;
             /* pass 2: max-shifted softmax */
             double m = -INFINITY;
             for (int64_t j = 0; j < nk; ++j) if (s[j] > m) m = s[j];
@@ -154,9 +164,10 @@ int oracle_attn_fwd(int64_t G, int64_t nq, int64_t nk, int64_t d,
  */
 int oracle_attn_fwd_online(int64_t G, int64_t nq, int64_t nk, int64_t d,
                            const double* q, const double* k, const double* v,
-                           const int64_t* qpos, int causal, int64_t wl, int64_t wr, double scale,
+                           const int64_t* qpos, int causal, int64_t wl, int64_t wr,
+                           const uint8_t* bm, int64_t bq, int64_t bk, int64_t nqb, int64_t nkb, double scale,
                            int64_t block, double* o, double* lse) {
-    const mask_t mk = {causal, wl, wr};
+    const mask_t mk = {causal, wl, wr, bm, bq, bk, nqb, nkb};
     if (block < 1) return -2;
     int failed = 0;
 #pragma omp parallel
@@ -182,7 +193,7 @@ int oracle_attn_fwd_online(int64_t G, int64_t nq, int64_t nk, int64_t d,
                 double m_local = -INFINITY;
                 for (int64_t t = 0; t < nb; ++t) {
                     int64_t j = j0 + t;
-                    s[t] = visible(mk, j, qpos[i]) ? scale * dot(qi, kg + j * d, d) : -INFINITY;
+                    s[t] = visible(mk, g, j, qpos[i]) ? scale * dot(qi, kg + j * d, d) : -INFINITY;
                     if (s[t] > m_local) m_local = s[t];
                 }
                 if (m_local == -INFINITY) continue; /* nothing visible in this block */
@@ -232,10 +243,11 @@ int oracle_attn_fwd_online(int64_t G, int64_t nq, int64_t nk, int64_t d,
  */
 int oracle_attn_bwd(int64_t G, int64_t nq, int64_t nk, int64_t d,
                     const double* q, const double* k, const double* v, const double* dout,
-                    const int64_t* qpos, int causal, int64_t wl, int64_t wr, double scale,
+                    const int64_t* qpos, int causal, int64_t wl, int64_t wr,
+                    const uint8_t* bm, int64_t bq, int64_t bk, int64_t nqb, int64_t nkb, double scale,
                     const int64_t* rows, int64_t nrows, double* dq,
                     const int64_t* keys, int64_t nkeys, double* dk, double* dv) {
-    const mask_t mk = {causal, wl, wr};
+    const mask_t mk = {causal, wl, wr, bm, bq, bk, nqb, nkb};
     if (rows == NULL) nrows = nq;
     if (keys == NULL) nkeys = nk;
     /* Which query rows need statistics: all of them if any key gradient is asked for. */
@@ -268,7 +280,7 @@ int oracle_attn_bwd(int64_t G, int64_t nq, int64_t nk, int64_t d,
             const double* vg = v + g * nk * d;
             double mi = -INFINITY;
             for (int64_t j = 0; j < nk; ++j) {
-                s[j] = visible(mk, j, qpos[i]) ? scale * dot(qi, kg + j * d, d) : -INFINITY;
+                s[j] = visible(mk, g, j, qpos[i]) ? scale * dot(qi, kg + j * d, d) : -INFINITY;
                 if (s[j] > mi) mi = s[j];
             }
             double li = 0.0, Di = 0.0;
@@ -305,7 +317,7 @@ int oracle_attn_bwd(int64_t G, int64_t nq, int64_t nk, int64_t d,
         for (int64_t c = 0; c < d; ++c) dqi[c] = 0.0;
         if (m[g * nq + i] == -INFINITY) continue; /* the row sees no key */
         for (int64_t j = 0; j < nk; ++j) {
-            if (!visible(mk, j, qpos[i])) continue;
+            if (!visible(mk, g, j, qpos[i])) continue;
             double p = exp(scale * dot(qi, kg + j * d, d) - m[g * nq + i]) / l[g * nq + i];
             double ds = p * (dot(doi, vg + j * d, d) - D[g * nq + i]);
             for (int64_t c = 0; c < d; ++c) dqi[c] += scale * ds * kg[j * d + c];
@@ -323,7 +335,7 @@ int oracle_attn_bwd(int64_t G, int64_t nq, int64_t nk, int64_t d,
         double* dvj = dv + (g * nkeys + jj) * d;
         for (int64_t c = 0; c < d; ++c) { dkj[c] = 0.0; dvj[c] = 0.0; }
         for (int64_t i = 0; i < nq; ++i) {
-            if (!visible(mk, j, qpos[i])) continue;
+            if (!visible(mk, g, j, qpos[i])) continue;
             const double* qi = q + (g * nq + i) * d;
             const double* doi = dout + (g * nq + i) * d;
             double p = exp(scale * dot(qi, kj, d) - m[g * nq + i]) / l[g * nq + i];

@@ -29,13 +29,18 @@ def rand(*shape, scale=1.0, rng=RNG):
 # independent scalar brute force (pure Python, exact summation with math.fsum)
 # ----------------------------------------------------------------------------
 
-def vis(j, pos, causal, window):
-    """Key j visible to a row at key position pos (independent restatement of the mask)."""
+def vis(j, pos, causal, window, bm=None, block=(1, 1)):
+    """Key j visible to a row at key position pos (independent restatement of the mask).
+
+    bm: optional block mask (nested lists or a 2-D array) indexed [pos // bq][j // bk]."""
     wl, wr = window
-    return (not causal or j <= pos) and (wl < 0 or j >= pos - wl) and (wr < 0 or j <= pos + wr)
+    ok = (not causal or j <= pos) and (wl < 0 or j >= pos - wl) and (wr < 0 or j <= pos + wr)
+    if ok and bm is not None:
+        ok = bool(bm[pos // block[0]][j // block[1]])
+    return ok
 
 
-def brute_fwd(q, k, v, causal, scale, window=(-1, -1)):
+def brute_fwd(q, k, v, causal, scale, window=(-1, -1), bm=None, block=(1, 1)):
     """O and lse of one head by the definition, scalar Python, math.fsum sums.
 
     Rows are aligned to the end of the keys (row i at key position i + nk - nq).
@@ -46,7 +51,7 @@ def brute_fwd(q, k, v, causal, scale, window=(-1, -1)):
     O, L = [], []
     for i in range(n):
         pos = i + nk - n
-        vis_j = [j for j in range(nk) if vis(j, pos, causal, window)]
+        vis_j = [j for j in range(nk) if vis(j, pos, causal, window, bm, block)]
         if not vis_j:
             O.append([0.0] * d)
             L.append(-math.inf)
@@ -60,7 +65,7 @@ def brute_fwd(q, k, v, causal, scale, window=(-1, -1)):
     return np.array(O), np.array(L)
 
 
-def brute_bwd_jacobian(q, k, v, do, causal, scale, window=(-1, -1)):
+def brute_bwd_jacobian(q, k, v, do, causal, scale, window=(-1, -1), bm=None, block=(1, 1)):
     """Gradients through the explicit softmax Jacobian dP_ij/dS_ij' = P_ij (delta_jj' - P_ij').
 
     A different route from the oracle's D-trick: it builds the full per-row
@@ -73,7 +78,7 @@ def brute_bwd_jacobian(q, k, v, do, causal, scale, window=(-1, -1)):
     dv = [[0.0] * d for _ in range(nk)]
     for i in range(n):
         pos = i + nk - n
-        vis_j = [j for j in range(nk) if vis(j, pos, causal, window)]
+        vis_j = [j for j in range(nk) if vis(j, pos, causal, window, bm, block)]
         if not vis_j:
             continue
         s = {j: scale * math.fsum(q[i][c] * k[j][c] for c in range(d)) for j in vis_j}
@@ -172,6 +177,26 @@ def pin_battery(lib):
             oo, ll = lib.fwd_online(q, k, v, causal, 0.8, 2, window=window)
             if relerr(oo, o) > 1e-12 or relerr(ll, lse) > 1e-12:
                 fails.append("online %dx%d window=%s causal=%d" % (nq, nk, window, causal))
+        # block masks with unequal block sides (one block row fully masked)
+        for (n, block) in ((9, (2, 3)), (8, (3, 2))):
+            d = 3
+            nqb, nkb = -(-n // block[0]), -(-n // block[1])
+            bm = (rng.random((nqb, nkb)) < 0.6).astype(np.uint8)
+            bm[1, :] = 0
+            q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+            o, lse = lib.fwd(q, k, v, causal, 0.9, block_mask=bm, block=block)
+            bo, bl = brute_fwd(q.tolist(), k.tolist(), v.tolist(), causal, 0.9, bm=bm, block=block)
+            if relerr(o[0], bo) > 1e-13 or relerr(lse[0], bl) > 1e-13:
+                fails.append("brute fwd block mask %s causal=%d" % (block, causal))
+            dq, dk, dv = lib.bwd(q, k, v, do, causal, 0.9, block_mask=bm, block=block)
+            bq, bk, bv = brute_bwd_jacobian(q.tolist(), k.tolist(), v.tolist(), do.tolist(), causal, 0.9,
+                                            bm=bm, block=block)
+            for name, a, b in (("dq", dq[0], bq), ("dk", dk[0], bk), ("dv", dv[0], bv)):
+                if relerr(a, b) > 1e-12:
+                    fails.append("brute %s block mask %s causal=%d" % (name, block, causal))
+            oo, ll = lib.fwd_online(q, k, v, causal, 0.9, 2, block_mask=bm, mask_block=block)
+            if relerr(oo, o) > 1e-12 or relerr(ll, lse) > 1e-12:
+                fails.append("online block mask %s causal=%d" % (block, causal))
     return fails
 
 
@@ -380,13 +405,13 @@ MUTANTS = {
     "lse_drops_max": ("lse[g * nq + i] = m + log(l);\n        }\n        free(s);",
                       "lse[g * nq + i] = log(l);\n        }\n        free(s);"),
     "unnormalised_weights": ("for (int64_t j = 0; j < nk; ++j) s[j] /= l;", ""),
-    "scale_dropped_in_scores": ("s[j] = visible(mk, j, qpos[i]) ? scale * dot(qi, kg + j * d, d) : -INFINITY;\n            /* pass 2",
-                                "s[j] = visible(mk, j, qpos[i]) ? dot(qi, kg + j * d, d) : -INFINITY;\n            /* pass 2"),
+    "scale_dropped_in_scores": ("s[j] = visible(mk, g, j, qpos[i]) ? scale * dot(qi, kg + j * d, d) : -INFINITY;\n            /* pass 2",
+                                "s[j] = visible(mk, g, j, qpos[i]) ? dot(qi, kg + j * d, d) : -INFINITY;\n            /* pass 2"),
     "online_no_output_rescale": ("for (int64_t c = 0; c < d; ++c) acc[c] *= alpha;", ""),
     "online_no_sum_rescale": ("l *= alpha;", ""),
     "window_left_off_by_one": ("if (mk.wl >= 0 && j < pos - mk.wl) return 0;", "if (mk.wl >= 0 && j <= pos - mk.wl) return 0;"),
     "window_right_ignored": ("if (mk.wr >= 0 && j > pos + mk.wr) return 0;", ""),
-    "bwd_ignores_qpos": ("if (!visible(mk, j, qpos[i])) continue;\n            const double* qi", "if (!visible(mk, j, i)) continue;\n            const double* qi"),
+    "bwd_ignores_qpos": ("if (!visible(mk, g, j, qpos[i])) continue;\n            const double* qi", "if (!visible(mk, g, j, i)) continue;\n            const double* qi"),
     "ds_sign": ("double ds = p * (dot(doi, vg + j * d, d) - D[g * nq + i]);",
                 "double ds = p * (D[g * nq + i] - dot(doi, vg + j * d, d));"),
     "D_missing_P": ("Di += s[j] * dp[j];", "Di += dp[j];"),
@@ -394,6 +419,9 @@ MUTANTS = {
     "dq_missing_scale": ("dqi[c] += scale * ds * kg[j * d + c];", "dqi[c] += ds * kg[j * d + c];"),
     "dv_uses_ds": ("dvj[c] += p * doi[c];", "dvj[c] += ds * doi[c];"),
     "dq_wrong_operand": ("dqi[c] += scale * ds * kg[j * d + c];", "dqi[c] += scale * ds * vg[j * d + c];"),
+    "block_key_index_uses_row_side": ("j / mk.bk]", "j / mk.bq]"),
+    "block_row_index_uses_key": ("pos / mk.bq)", "j / mk.bq)"),
+    "block_mask_inverted": ("if (mk.bm && !mk.bm[", "if (mk.bm && mk.bm["),
 }
 
 
@@ -497,3 +525,58 @@ def test_varlen_against_block_diagonal_torch(causal, window):
     assert relerr(dk, np.where(np.isnan(tdk), 0.0, tdk)) <= 1e-11
     assert relerr(dv, np.where(np.isnan(tdv), 0.0, tdv)) <= 1e-11
     assert np.all(o[:, ~seen] == 0.0) and np.all(l[:, ~seen] == -np.inf)
+
+
+# ----------------------------------------------------------------------------
+# block masks
+# ----------------------------------------------------------------------------
+
+def _block_mask_matrix(n, bm, block, causal):
+    pos = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    m = bm[pos // block[0], j // block[1]] != 0
+    if causal:
+        m &= j <= pos
+    return m
+
+
+@pytest.mark.parametrize("n,block,causal", [(300, (128, 128), False), (300, (128, 128), True),
+                                            (257, (64, 32), True), (200, (32, 96), False)])
+def test_block_mask_against_torch_masked(n, block, causal):
+    G, d, scale = 2, 16, 0.3
+    rng = np.random.default_rng(n + block[0])
+    nqb, nkb = -(-n // block[0]), -(-n // block[1])
+    bm = (rng.random((G, nqb, nkb)) < 0.5).astype(np.uint8)
+    bm[:, :, 0] = 1       # most rows see something ...
+    bm[0, 1, :] = 0       # ... but one block row of head 0 sees nothing
+    q, k, v, do = rand(G, n, d), rand(G, n, d), rand(G, n, d), rand(G, n, d)
+    o, l = oracle.fwd(q, k, v, causal, scale, block_mask=bm, block=block)
+    dq, dk, dv = oracle.bwd(q, k, v, do, causal, scale, block_mask=bm, block=block)
+    for g in range(G):
+        mask = _block_mask_matrix(n, bm[g], block, causal)
+        seen = mask.any(axis=1)
+        to, tl, tdq, tdk, tdv = _torch_masked(q[g:g + 1], k[g:g + 1], v[g:g + 1], do[g:g + 1], mask, scale)
+        assert relerr(o[g, seen], to[0, seen]) <= 1e-12 and relerr(l[g, seen], tl[0, seen]) <= 1e-12
+        assert relerr(dq[g, seen], tdq[0, seen]) <= 1e-11
+        assert relerr(dk[g], np.where(np.isnan(tdk[0]), 0.0, tdk[0])) <= 1e-11
+        assert relerr(dv[g], np.where(np.isnan(tdv[0]), 0.0, tdv[0])) <= 1e-11
+        assert np.all(o[g, ~seen] == 0.0) and np.all(l[g, ~seen] == -np.inf) and np.all(dq[g, ~seen] == 0.0)
+    assert (~_block_mask_matrix(n, bm[0], block, causal).any(axis=1)).any()  # the empty rows were exercised
+
+
+def test_block_mask_all_ones_and_block_causal():
+    n, d = 200, 8
+    q, k, v = rand(1, n, d), rand(1, n, d), rand(1, n, d)
+    ones = np.ones((2, 4), np.uint8)
+    for causal in (False, True):
+        o1, l1 = oracle.fwd(q, k, v, causal, 0.5)
+        o2, l2 = oracle.fwd(q, k, v, causal, 0.5, block_mask=ones, block=(128, 64))
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # causal inside a lower-triangular block mask of square blocks is just causal
+    tri = np.tril(np.ones((4, 4), np.uint8))
+    o1, l1 = oracle.fwd(q, k, v, True, 0.5)
+    o2, l2 = oracle.fwd(q, k, v, True, 0.5, block_mask=tri, block=(64, 64))
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # an all-zero mask: no row sees a key
+    o3, l3 = oracle.fwd(q, k, v, False, 0.5, block_mask=np.zeros((2, 2), np.uint8), block=(128, 128))
+    assert np.all(o3 == 0.0) and np.all(l3 == -np.inf)
