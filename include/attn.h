@@ -47,6 +47,7 @@
 #define IO_AWARE_EXACT_ATTN_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -101,6 +102,38 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              const float* lse, void* dq, void* dk, void* dv,
              int B, int H, int N, int d, int causal, float scale, int dtype,
              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Block-sparse attention: the tile skipping of all-zero mask blocks that the
+ * snabindia page describes (chapter 1 and section 3.1), with the mask given
+ * explicitly.  The key and query sequences are cut into blocks of
+ * ATTN_MASK_BLOCK = 128 positions; key j is visible from query i only if
+ * block_mask[m][i / 128][j / 128] != 0 (and, with causal = 1, j <= i).  Pairs
+ * of blocks whose byte is 0 are never loaded or computed; the result is exact
+ * attention under that mask.  A query row that sees no key gets O = 0 and
+ * lse = -inf (and dQ = 0).
+ *   block_mask : device bytes [mask_heads, nb, nb], nb = ceil(N / 128),
+ *                row-major, owned by the caller, read-only (no alignment
+ *                requirement); must not overlap any output.
+ *   mask_heads : 1 (one mask for every batch and head), H (one per head,
+ *                shared by the batches) or B*H (one per batch and head:
+ *                m = b*H + h); anything else returns ATTN_E_SHAPE.
+ * All other arguments, layouts and errors are those of attn_fwd / attn_bwd;
+ * a NULL block_mask with B*H*N > 0 returns ATTN_E_NULL.  The backward takes
+ * the same mask as the forward whose o and lse it is given, and the same
+ * workspace as attn_bwd (attn_bwd_workspace_bytes).
+ */
+#define ATTN_MASK_BLOCK 128
+
+int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int H, int N, int d, const uint8_t* block_mask, int mask_heads,
+                         int causal, float scale, int dtype, void* stream);
+
+int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                         const float* lse, void* dq, void* dk, void* dv,
+                         int B, int H, int N, int d, const uint8_t* block_mask, int mask_heads,
+                         int causal, float scale, int dtype,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Packed variable-length batches, rectangular shapes and sliding windows.

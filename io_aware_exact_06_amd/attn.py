@@ -24,7 +24,9 @@ STATUS = {
 }
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_string",
            "attn_fwd_varlen", "attn_bwd_varlen", "attn_bwd_varlen_workspace_bytes",
-           "attn_fwd_unfused", "attn_fwd_unfused_workspace_bytes")
+           "attn_fwd_unfused", "attn_fwd_unfused_workspace_bytes",
+           "attn_fwd_blocksparse", "attn_bwd_blocksparse")
+MASK_BLOCK = 128  # ATTN_MASK_BLOCK
 
 _lib = None
 
@@ -63,6 +65,11 @@ def lib() -> ctypes.CDLL:
         L.attn_fwd_unfused_workspace_bytes.restype = sz
         L.attn_fwd_unfused.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
         L.attn_fwd_unfused.restype = i
+        L.attn_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, vp, i, i, f, i, vp]
+        L.attn_fwd_blocksparse.restype = i
+        L.attn_bwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, i, i, f, i, vp, sz,
+                                           vp]
+        L.attn_bwd_blocksparse.restype = i
         _lib = L
     return _lib
 
@@ -103,6 +110,18 @@ def attn_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, cu_q, cu_k, batch, H, tot
     return lib().attn_bwd_varlen(q, k, v, o, dout, lse, dq, dk, dv, cu_q, cu_k, batch, H, total_q, total_k,
                                  max_q, max_k, d, int(causal), window_left, window_right, float(scale), dtype,
                                  workspace, workspace_bytes, stream)
+
+
+def attn_fwd_blocksparse(q, k, v, o, lse, B, H, N, d, block_mask, mask_heads, causal, scale, dtype,
+                         stream) -> int:
+    return lib().attn_fwd_blocksparse(q, k, v, o, lse, B, H, N, d, block_mask, mask_heads, int(causal),
+                                      float(scale), dtype, stream)
+
+
+def attn_bwd_blocksparse(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, block_mask, mask_heads, causal, scale,
+                         dtype, workspace, workspace_bytes, stream) -> int:
+    return lib().attn_bwd_blocksparse(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, block_mask, mask_heads,
+                                      int(causal), float(scale), dtype, workspace, workspace_bytes, stream)
 
 
 def _check(status: int):
@@ -257,3 +276,54 @@ def fwd_unfused(q, k, v, causal: bool = False, scale: float | None = None, o=Non
                             causal, scale, _dtype_code(q), workspace.data_ptr(), workspace.numel(),
                             _stream_handle(q.device)))
     return o, lse
+
+
+def _block_mask(block_mask, B, H, N, device):
+    """Device uint8 copy of a [nb, nb], [H, nb, nb] or [B*H, nb, nb] block mask; returns (tensor, mask_heads)."""
+    import torch
+    nb = (N + MASK_BLOCK - 1) // MASK_BLOCK
+    m = torch.as_tensor(block_mask)
+    if m.dim() == 2:
+        m = m.unsqueeze(0)
+    if m.dim() != 3 or m.shape[1:] != (nb, nb) or m.shape[0] not in (1, H, B * H):
+        raise ValueError("block mask must be [nb, nb], [H, nb, nb] or [B*H, nb, nb] with nb = %d" % nb)
+    m = (m != 0).to(device=device, dtype=torch.uint8).contiguous()
+    return m, int(m.shape[0])
+
+
+def fwd_blocksparse(q, k, v, block_mask, causal: bool = False, scale: float | None = None, o=None, lse=None):
+    """O, lse of attention restricted to the active 128 x 128 blocks of block_mask."""
+    import torch
+    B, H, N, d = _shape(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    m, mh = _block_mask(block_mask, B, H, N, q.device)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check(attn_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                B, H, N, d, m.data_ptr(), mh, causal, scale, _dtype_code(q),
+                                _stream_handle(q.device)))
+    return o, lse
+
+
+def bwd_blocksparse(q, k, v, o, dout, lse, block_mask, causal: bool = False, scale: float | None = None,
+                    dq=None, dk=None, dv=None, workspace=None):
+    """dq, dk, dv of block-sparse attention (same mask as the forward)."""
+    import torch
+    B, H, N, d = _shape(q, k, v, o, dout)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    m, mh = _block_mask(block_mask, B, H, N, q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    need = attn_bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(attn_bwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
+                                m.data_ptr(), mh, causal, scale, _dtype_code(q), workspace.data_ptr(),
+                                workspace.numel(), _stream_handle(q.device)))
+    return dq, dk, dv

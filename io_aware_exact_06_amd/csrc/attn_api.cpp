@@ -61,12 +61,37 @@ const char* attn_status_string(int status) {
     }
 }
 
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
-             int d, int causal, float scale, int dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Bytes of a block mask [mask_heads, nb, nb], nb = ceil(N / 128); 0 when the
+// call's mask_heads is not 1, H or B*H.
+size_t mask_bytes(int B, int H, int N, int mask_heads) {
+    const int64_t bh = (int64_t)B * H;
+    if (mask_heads != 1 && mask_heads != H && mask_heads != bh) return 0;
+    if (mask_heads <= 0) return 0;
+    const int64_t nb = ((int64_t)N + attn::kMaskBlock - 1) / attn::kMaskBlock;
+    return (size_t)mask_heads * (size_t)nb * (size_t)nb;
+}
+
+attn::SeqLayout dense_layout(int B, int H, int N, int causal, const uint8_t* bm, int mask_heads) {
+    attn::SeqLayout L{0, B, H, N, nullptr, nullptr, N, N, -1, causal ? 0 : -1, bm, mask_heads,
+                      (N + attn::kMaskBlock - 1) / attn::kMaskBlock};
+    return L;
+}
+
+int fwd_dense(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+              const uint8_t* bm, int mask_heads, int causal, float scale, int dtype, void* stream) {
     int64_t rows = 0, elems = 0;
     int st = check_common(B, H, N, d, causal, scale, dtype, &rows, &elems);
     if (st != ATTN_OK) return st;
     if (rows == 0) return ATTN_OK;
+    size_t mb = 0;
+    if (bm) {
+        mb = mask_bytes(B, H, N, mask_heads);
+        if (mb == 0) return ATTN_E_SHAPE;
+    }
     if (!q || !k || !v || !o || !lse) return ATTN_E_NULL;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
         return ATTN_E_ALIGN;
@@ -76,9 +101,61 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv) || overlap(rl, rq) || overlap(rl, rk) ||
         overlap(rl, rv) || overlap(ro, rl))
         return ATTN_E_ALIAS;
-    attn::SeqLayout L{0, B, H, N, nullptr, nullptr, N, N, -1, causal ? 0 : -1};
-    attn::FwdParams p{q, k, v, o, lse, L, N, d, dtype, scale, stream};
+    if (bm && (overlap(ro, range_of(bm, mb)) || overlap(rl, range_of(bm, mb)))) return ATTN_E_ALIAS;
+    attn::FwdParams p{q, k, v, o, lse, dense_layout(B, H, N, causal, bm, mask_heads), N, d, dtype, scale, stream};
     return attn::launch_fwd(p) == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+int bwd_dense(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+              void* dq, void* dk, void* dv, int B, int H, int N, int d, const uint8_t* bm, int mask_heads,
+              int causal, float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    int64_t rows = 0, elems = 0;
+    int st = check_common(B, H, N, d, causal, scale, dtype, &rows, &elems);
+    if (st != ATTN_OK) return st;
+    if (rows == 0) return ATTN_OK;
+    size_t mb = 0;
+    if (bm) {
+        mb = mask_bytes(B, H, N, mask_heads);
+        if (mb == 0) return ATTN_E_SHAPE;
+    }
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_E_NULL;
+    if (!workspace) return ATTN_E_WORKSPACE;
+    const void* a16[] = {q, k, v, o, dout, dq, dk, dv, workspace};
+    for (const void* p : a16)
+        if (!aligned(p, 16)) return ATTN_E_ALIGN;
+    if (!aligned(lse, 4)) return ATTN_E_ALIGN;
+    const size_t ws_need = attn::bwd_workspace_bytes_rows(rows);
+    if (workspace_bytes < ws_need) return ATTN_E_WORKSPACE;
+    const size_t tb = (size_t)elems * 2, lb = (size_t)rows * 4;
+    const Range ins[] = {range_of(q, tb), range_of(k, tb), range_of(v, tb), range_of(o, tb),
+                         range_of(dout, tb), range_of(lse, lb), range_of(bm, mb)};
+    const Range outs[] = {range_of(dq, tb), range_of(dk, tb), range_of(dv, tb),
+                          range_of(workspace, ws_need)};
+    for (int i = 0; i < 4; ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r)) return i == 3 ? ATTN_E_WORKSPACE : ATTN_E_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlap(outs[i], outs[j])) return j == 3 ? ATTN_E_WORKSPACE : ATTN_E_ALIAS;
+    }
+    attn::BwdParams p{q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace,
+                      dense_layout(B, H, N, causal, bm, mask_heads), N, N, d, dtype, scale, stream};
+    return attn::launch_bwd(p) == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+             int d, int causal, float scale, int dtype, void* stream) {
+    return fwd_dense(q, k, v, o, lse, B, H, N, d, nullptr, 0, causal, scale, dtype, stream);
+}
+
+int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                         int d, const uint8_t* block_mask, int mask_heads, int causal, float scale, int dtype,
+                         void* stream) {
+    if ((int64_t)B * H * N > 0 && !block_mask) return ATTN_E_NULL;
+    return fwd_dense(q, k, v, o, lse, B, H, N, d, block_mask, mask_heads, causal, scale, dtype, stream);
 }
 
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d) {
@@ -91,32 +168,17 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N, int d) {
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
              const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal,
              float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-    int64_t rows = 0, elems = 0;
-    int st = check_common(B, H, N, d, causal, scale, dtype, &rows, &elems);
-    if (st != ATTN_OK) return st;
-    if (rows == 0) return ATTN_OK;
-    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_E_NULL;
-    if (!workspace) return ATTN_E_WORKSPACE;
-    const void* a16[] = {q, k, v, o, dout, dq, dk, dv, workspace};
-    for (const void* p : a16)
-        if (!aligned(p, 16)) return ATTN_E_ALIGN;
-    if (!aligned(lse, 4)) return ATTN_E_ALIGN;
-    const size_t ws_need = attn::bwd_workspace_bytes_rows(rows);
-    if (workspace_bytes < ws_need) return ATTN_E_WORKSPACE;
-    const size_t tb = (size_t)elems * 2, lb = (size_t)rows * 4;
-    const Range ins[] = {range_of(q, tb), range_of(k, tb), range_of(v, tb), range_of(o, tb),
-                         range_of(dout, tb), range_of(lse, lb)};
-    const Range outs[] = {range_of(dq, tb), range_of(dk, tb), range_of(dv, tb),
-                          range_of(workspace, ws_need)};
-    for (int i = 0; i < 4; ++i) {
-        for (const Range& r : ins)
-            if (overlap(outs[i], r)) return i == 3 ? ATTN_E_WORKSPACE : ATTN_E_ALIAS;
-        for (int j = i + 1; j < 4; ++j)
-            if (overlap(outs[i], outs[j])) return j == 3 ? ATTN_E_WORKSPACE : ATTN_E_ALIAS;
-    }
-    attn::SeqLayout L{0, B, H, N, nullptr, nullptr, N, N, -1, causal ? 0 : -1};
-    attn::BwdParams p{q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, L, N, N, d, dtype, scale, stream};
-    return attn::launch_bwd(p) == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+    return bwd_dense(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, nullptr, 0, causal, scale, dtype, workspace,
+                     workspace_bytes, stream);
+}
+
+int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                         const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                         const uint8_t* block_mask, int mask_heads, int causal, float scale, int dtype,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    if ((int64_t)B * H * N > 0 && !block_mask) return ATTN_E_NULL;
+    return bwd_dense(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, block_mask, mask_heads, causal, scale, dtype,
+                     workspace, workspace_bytes, stream);
 }
 
 namespace {
@@ -138,7 +200,7 @@ int check_varlen(const int* cu_q, const int* cu_k, int batch, int H, int total_q
 
 attn::SeqLayout varlen_layout(const int* cu_q, const int* cu_k, int batch, int H, int total_q, int total_k,
                               int causal, int wl, int wr) {
-    return attn::SeqLayout{1, batch, H, 0, cu_q, cu_k, total_q, total_k, wl, causal ? 0 : wr};
+    return attn::SeqLayout{1, batch, H, 0, cu_q, cu_k, total_q, total_k, wl, causal ? 0 : wr, nullptr, 0, 0};
 }
 
 }  // namespace

@@ -96,7 +96,7 @@ __device__ inline void store_staged(uint16_t* __restrict__ dst, const uint16_t* 
 constexpr int kQ_BQ = 128;
 constexpr int kQ_BK = 64;
 
-template <class T, int D>
+template <class T, int D, bool BS>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                         const uint16_t* __restrict__ V, const uint16_t* __restrict__ O,
@@ -150,9 +150,23 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     const TileRange tr = tile_range(sq.key_lo(q0), sq.key_hi(qlast), sq.key_lo(qlast),
                                     min(sq.key_hi(q0), nk - 1), nk, kQ_BK);
     const uint32_t goff = DT::lane_goff(lane);
-    if (tr.end > tr.first) {
-        dma_tile<D, kQ_BK>(Kh, tr.first * kQ_BK, nk, Ks + (tr.first & 1) * TB, w, lane, goff);
-        dma_tile<D, kQ_BK>(Vh, tr.first * kQ_BK, nk, Vs + (tr.first & 1) * TB, w, lane, goff);
+    // With a block mask only the key tiles of active (query block, key block)
+    // pairs are visited (a 64-key tile lies in mask block t / 2; the mask is
+    // read with uniform loads).
+    static_assert(!BS || (kQ_BQ == kMaskBlock && 2 * kQ_BK == kMaskBlock), "block masks need 128-row groups");
+    const uint8_t* bmrow = BS ? sq.bm + (size_t)(q0 / kMaskBlock) * sq.nb : nullptr;
+    auto next_tile = [&](int t) __attribute__((always_inline)) {
+        ++t;
+        if (BS)
+            while (t < tr.end && !bmrow[t >> 1]) ++t;
+        return t;
+    };
+    int j0 = tr.first;
+    if (BS)
+        while (j0 < tr.end && !bmrow[j0 >> 1]) ++j0;
+    if (j0 < tr.end) {
+        dma_tile<D, kQ_BK>(Kh, j0 * kQ_BK, nk, Ks, w, lane, goff);
+        dma_tile<D, kQ_BK>(Vh, j0 * kQ_BK, nk, Vs, w, lane, goff);
     }
     // Unconditional: the fragments above and the first tiles have landed (the
     // compiler counts only its own loads; see the forward kernel).
@@ -167,14 +181,14 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     const uint32_t fo[2] = {DT::frag_lane(lane, 0), DT::frag_lane(lane, 1)};
     const uint32_t to0 = DT::tr_lane(lane, 0), to1 = DT::tr_lane(lane, 1);
 
-    auto step = [&](int jt, auto masked_tag) __attribute__((always_inline)) {
+    // Tile jt in buffer buf; jn is the next tile visited.
+    auto step = [&](int jt, int jn, int buf, auto masked_tag) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_tag)::value;
-        const int buf = jt & 1;
         const int k0 = jt * kQ_BK;
-        // the other buffers held tile jt-1, which every wave has finished
-        if (jt + 1 < tr.end) {
-            dma_tile<D, kQ_BK>(Kh, k0 + kQ_BK, nk, Ks + (1 - buf) * TB, w, lane, goff);
-            dma_tile<D, kQ_BK>(Vh, k0 + kQ_BK, nk, Vs + (1 - buf) * TB, w, lane, goff);
+        // the other buffers held the previous tile, which every wave has finished
+        if (jn < tr.end) {
+            dma_tile<D, kQ_BK>(Kh, jn * kQ_BK, nk, Ks + (1 - buf) * TB, w, lane, goff);
+            dma_tile<D, kQ_BK>(Vh, jn * kQ_BK, nk, Vs + (1 - buf) * TB, w, lane, goff);
         }
         if (!MASKED || (wq0 < nq && k0 <= sq.key_hi(wq0 + 31) && k0 + kQ_BK - 1 >= sq.key_lo(wq0))) {
             const char* kt = (const char*)(Ks + buf * TB);
@@ -231,9 +245,18 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
         wait_dma();
         __syncthreads();
     };
-    for (int jt = tr.first; jt < tr.full_first; ++jt) step(jt, Flag<true>{});
-    for (int jt = tr.full_first; jt < tr.full_end; ++jt) step(jt, Flag<false>{});
-    for (int jt = tr.full_end; jt < tr.end; ++jt) step(jt, Flag<true>{});
+    if constexpr (!BS) {
+        for (int jt = tr.first; jt < tr.full_first; ++jt) step(jt, jt + 1, jt - tr.first & 1, Flag<true>{});
+        for (int jt = tr.full_first; jt < tr.full_end; ++jt) step(jt, jt + 1, jt - tr.first & 1, Flag<false>{});
+        for (int jt = tr.full_end; jt < tr.end; ++jt) step(jt, jt + 1, jt - tr.first & 1, Flag<true>{});
+    } else {
+        for (int jt = j0, buf = 0; jt < tr.end; buf ^= 1) {
+            const int jn = next_tile(jt);
+            if (jt < tr.full_first || jt >= tr.full_end) step(jt, jn, buf, Flag<true>{});
+            else step(jt, jn, buf, Flag<false>{});
+            jt = jn;
+        }
+    }
 
     stage_transposed<T, D, STR>(smem, 32 * w + n32, h, dqacc, scale);
     __syncthreads();
@@ -250,7 +273,7 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 constexpr int kK_BK = 128;
 constexpr int kK_BQ = 64;
 
-template <class T, int D>
+template <class T, int D, bool BS>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(D == 64 ? 2 : 1, 2)))
 void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -314,12 +337,27 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
             stats[sb][1][tid] = st_d;
         }
     };
-    if (tr.end > tr.first) {
-        const int r0 = tr.first * kK_BQ, sb0 = tr.first & 1;
-        dma_tile<D, kK_BQ>(Qh, r0, nq, Qs + sb0 * TB, w, lane, goff);
-        dma_tile<D, kK_BQ>(dOh, r0, nq, dOs + sb0 * TB, w, lane, goff);
+    // With a block mask only the query tiles of active (query block, key
+    // block) pairs are visited: a 64-row tile lies in mask block t / 2, and
+    // this group's 128 keys are key block kt (the mask column is read with
+    // uniform loads).
+    static_assert(!BS || (kK_BK == kMaskBlock && 2 * kK_BQ == kMaskBlock), "block masks need 128-key groups");
+    const uint8_t* bmcol = BS ? sq.bm + kt : nullptr;
+    auto next_tile = [&](int t) __attribute__((always_inline)) {
+        ++t;
+        if (BS)
+            while (t < tr.end && !bmcol[(size_t)(t >> 1) * sq.nb]) ++t;
+        return t;
+    };
+    int i0 = tr.first;
+    if (BS)
+        while (i0 < tr.end && !bmcol[(size_t)(i0 >> 1) * sq.nb]) ++i0;
+    if (i0 < tr.end) {
+        const int r0 = i0 * kK_BQ;
+        dma_tile<D, kK_BQ>(Qh, r0, nq, Qs, w, lane, goff);
+        dma_tile<D, kK_BQ>(dOh, r0, nq, dOs, w, lane, goff);
         load_stats(r0);
-        store_stats(sb0);
+        store_stats(0);
     }
     wait_dma();  // unconditional (see the dq kernel)
     __syncthreads();
@@ -335,16 +373,16 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     const uint32_t fo[2] = {DT::frag_lane(lane, 0), DT::frag_lane(lane, 1)};
     const uint32_t to0 = DT::tr_lane(lane, 0), to1 = DT::tr_lane(lane, 1);
 
-    auto step = [&](int it, auto masked_tag) __attribute__((always_inline)) {
+    // Query tile it in buffer sb; in is the next tile visited.
+    auto step = [&](int it, int in, int sb, auto masked_tag) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_tag)::value;
-        const int sb = it & 1;
         const int qq0 = it * kK_BQ;
-        const bool more = it + 1 < tr.end;
-        // the other buffers held tile it-1, which every wave has finished
+        const bool more = in < tr.end;
+        // the other buffers held the previous tile, which every wave has finished
         if (more) {
-            dma_tile<D, kK_BQ>(Qh, qq0 + kK_BQ, nq, Qs + (1 - sb) * TB, w, lane, goff);
-            dma_tile<D, kK_BQ>(dOh, qq0 + kK_BQ, nq, dOs + (1 - sb) * TB, w, lane, goff);
-            load_stats(qq0 + kK_BQ);
+            dma_tile<D, kK_BQ>(Qh, in * kK_BQ, nq, Qs + (1 - sb) * TB, w, lane, goff);
+            dma_tile<D, kK_BQ>(dOh, in * kK_BQ, nq, dOs + (1 - sb) * TB, w, lane, goff);
+            load_stats(in * kK_BQ);
         }
         const char* qt_ = (const char*)(Qs + sb * TB);
         const char* ot_ = (const char*)(dOs + sb * TB);
@@ -408,14 +446,23 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
             sched_reads_ahead<8, DB * 4, 2>();
             prio_normal();
         }
-        // stats[sb ^ 1] held tile it-1's statistics, which every wave has finished
+        // stats[sb ^ 1] held the previous tile's statistics, which every wave has finished
         if (more) store_stats(sb ^ 1);
         wait_dma();
         __syncthreads();
     };
-    for (int it = tr.first; it < tr.full_first; ++it) step(it, Flag<true>{});
-    for (int it = tr.full_first; it < tr.full_end; ++it) step(it, Flag<false>{});
-    for (int it = tr.full_end; it < tr.end; ++it) step(it, Flag<true>{});
+    if constexpr (!BS) {
+        for (int it = tr.first; it < tr.full_first; ++it) step(it, it + 1, it - tr.first & 1, Flag<true>{});
+        for (int it = tr.full_first; it < tr.full_end; ++it) step(it, it + 1, it - tr.first & 1, Flag<false>{});
+        for (int it = tr.full_end; it < tr.end; ++it) step(it, it + 1, it - tr.first & 1, Flag<true>{});
+    } else {
+        for (int it = i0, sb = 0; it < tr.end; sb ^= 1) {
+            const int in = next_tile(it);
+            if (it < tr.full_first || it >= tr.full_end) step(it, in, sb, Flag<true>{});
+            else step(it, in, sb, Flag<false>{});
+            it = in;
+        }
+    }
 
     stage_transposed<T, D, STR>(smem, 32 * w + n32, h, dkacc, scale);
     __syncthreads();
@@ -426,7 +473,7 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     store_staged<D, STR>(dV + sq.krow0 * D, smem, kK_BK, k0, nk, tid);
 }
 
-template <class T, int D>
+template <class T, int D, bool BS>
 hipError_t launch(const BwdParams& p) {
     const int ntq = (p.max_nq + kQ_BQ - 1) / kQ_BQ;
     const int ntk = (p.max_nk + kK_BK - 1) / kK_BK;
@@ -435,29 +482,30 @@ hipError_t launch(const BwdParams& p) {
     const float c = p.scale * kLog2e;
     hipStream_t st = (hipStream_t)p.stream;
     if (nseq * ntq > 0) {
-        hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D>), dim3((unsigned)(nseq * ntq)), dim3(kThreads), 0, st,
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<T, D, BS>), dim3((unsigned)(nseq * ntq)), dim3(kThreads), 0, st,
                            (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v, (const uint16_t*)p.o,
                            (const uint16_t*)p.dout, p.lse, p.delta, (uint16_t*)p.dq, p.L, ntq, p.scale, c);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (nseq * ntk > 0) {
-        hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D>), dim3((unsigned)(nseq * ntk)), dim3(kThreads), 0, st,
+        hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, D, BS>), dim3((unsigned)(nseq * ntk)), dim3(kThreads), 0, st,
                            (const uint16_t*)p.q, (const uint16_t*)p.k, (const uint16_t*)p.v, (const uint16_t*)p.dout,
                            p.lse, p.delta, (uint16_t*)p.dk, (uint16_t*)p.dv, p.L, ntk, p.scale, c);
     }
     return hipGetLastError();
 }
 
-template <class T>
+template <class T, bool BS>
 hipError_t launch_d(const BwdParams& p) {
-    return p.d == 64 ? launch<T, 64>(p) : launch<T, 128>(p);
+    return p.d == 64 ? launch<T, 64, BS>(p) : launch<T, 128, BS>(p);
 }
 
 }  // namespace
 
 hipError_t launch_bwd(const BwdParams& p) {
-    return p.dtype == kDtypeBF16 ? launch_d<BF16>(p) : launch_d<F16>(p);
+    if (p.L.bmask) return p.dtype == kDtypeBF16 ? launch_d<BF16, true>(p) : launch_d<F16, true>(p);
+    return p.dtype == kDtypeBF16 ? launch_d<BF16, false>(p) : launch_d<F16, false>(p);
 }
 
 }  // namespace attn

@@ -306,6 +306,8 @@ struct Seq {
     int nq, nk;
     int off;     // query row i sits at key position i + off
     int wl, wr;  // window bounds (-1: unbounded)
+    const uint8_t* bm;  // block mask of this sequence, [nb, nb] (nullptr: none)
+    int nb;
 
     // First and last key (inclusive, before clipping to [0, nk)) visible to row i.
     __device__ inline int key_lo(int i) const { return wl < 0 ? -0x3fffffff : i + off - wl; }
@@ -322,10 +324,16 @@ __device__ inline Seq resolve(const SeqLayout& L, int s) {
     Seq r;
     r.wl = L.wl;
     r.wr = L.wr;
+    r.bm = nullptr;
+    r.nb = L.bm_nb;
     if (L.mode == 0) {
         r.qrow0 = r.krow0 = (int64_t)s * L.N;
         r.nq = r.nk = L.N;
         r.off = 0;
+        if (L.bmask) {
+            const int m = L.bm_heads == 1 ? 0 : (L.bm_heads == L.H ? s % L.H : s);
+            r.bm = L.bmask + (size_t)m * L.bm_nb * L.bm_nb;
+        }
         return r;
     }
     const int h = s / L.B, b = s % L.B;

@@ -55,9 +55,23 @@ constexpr int kBK = 64;        // key rows per tile
 #endif
 constexpr float kLazy = 8.0f;  // rescale only when the maximum grows by more than 2^8
 
-template <class T, int D, int QB>
+// Maximum of 32 values as a tree of three-input maxima (depth 4 instead of a
+// 31-long dependent chain).
+__device__ inline float max32(const f32x16& a, const f32x16& b) {
+    float t[11];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) t[i] = fmaxf(fmaxf(a[3 * i], a[3 * i + 1]), a[3 * i + 2]);
+#pragma unroll
+    for (int i = 0; i < 5; ++i) t[5 + i] = fmaxf(fmaxf(b[3 * i], b[3 * i + 1]), b[3 * i + 2]);
+    t[10] = fmaxf(a[15], b[15]);
+    const float u0 = fmaxf(fmaxf(t[0], t[1]), t[2]), u1 = fmaxf(fmaxf(t[3], t[4]), t[5]);
+    const float u2 = fmaxf(fmaxf(t[6], t[7]), t[8]), u3 = fmaxf(t[9], t[10]);
+    return fmaxf(fmaxf(u0, u1), fmaxf(u2, u3));
+}
+
+template <class T, int D, int QB, bool BS>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(QB == 1 ? 2 : 1, QB == 1 ? 2 : 1)))
+                          amdgpu_waves_per_eu(QB == 1 && !BS ? 2 : 1, QB == 1 && !BS ? 2 : 1)))
 void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                      float* __restrict__ LSE, SeqLayout L, int ntq, float scale, float c) {
@@ -143,12 +157,29 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             }
     };
 
-    // Prologue: tiles first (K, V) and first+1 (K) in flight, then the scores of the first.
-    if (tr.end > tr.first) {
-        dma_tile<D, kBK>(Kh, tr.first * kBK, nk, Kb + (tr.first & 1) * TB, w, lane, goff);
-        dma_tile<D, kBK>(Vh, tr.first * kBK, nk, Vb + (tr.first & 1) * TB, w, lane, goff);
-        if (tr.first + 1 < tr.end)
-            dma_tile<D, kBK>(Kh, (tr.first + 1) * kBK, nk, Kb + ((tr.first + 1) & 1) * TB, w, lane, goff);
+    // With a block mask, only the key tiles of active (query block, key block)
+    // pairs are visited, in order; the buffer parity then follows the position
+    // in that walk instead of the tile index.  The mask is read with uniform
+    // (scalar) loads.  A tile of 64 keys lies in mask block t / 2.
+    static_assert(!BS || (BQ == kMaskBlock && 2 * kBK == kMaskBlock), "block masks need 128-row groups");
+    const uint8_t* bmrow = BS ? sq.bm + (size_t)(q0 / kMaskBlock) * sq.nb : nullptr;
+    auto next_tile = [&](int t) __attribute__((always_inline)) {
+        ++t;
+        if (BS)
+            while (t < tr.end && !bmrow[t >> 1]) ++t;
+        return t;
+    };
+    int j0 = tr.first;
+    if (BS)
+        while (j0 < tr.end && !bmrow[j0 >> 1]) ++j0;
+    const int j1 = j0 < tr.end ? next_tile(j0) : tr.end;
+    const int p0 = BS ? 0 : (j0 & 1);  // buffer parity of the first tile
+
+    // Prologue: tiles j0 (K, V) and j1 (K) in flight, then the scores of j0.
+    if (j0 < tr.end) {
+        dma_tile<D, kBK>(Kh, j0 * kBK, nk, Kb + p0 * TB, w, lane, goff);
+        dma_tile<D, kBK>(Vh, j0 * kBK, nk, Vb + p0 * TB, w, lane, goff);
+        if (j1 < tr.end) dma_tile<D, kBK>(Kh, j1 * kBK, nk, Kb + (1 - p0) * TB, w, lane, goff);
     }
     // Unconditional: the Q fragments and the first tiles have landed.  The
     // compiler counts only its own loads in vmcnt; waiting for everything
@@ -156,25 +187,27 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     // loop, where the hardware counter also holds the prefetch DMA.
     wait_dma();
     __syncthreads();
-    if (tr.end > tr.first) {
-        if (tr.first & 1) scores(Flag<1>{});
+    if (j0 < tr.end) {
+        if (p0) scores(Flag<1>{});
         else scores(Flag<0>{});
     }
 
-    // One key tile jt (parity PAR): its scores are in sacc[PAR]; K(jt+1) and
-    // V(jt) are in LDS.  MASKED: the tile crosses the edge of some row's
-    // visible band.  NEXT: a tile jt+1 exists.
-    auto step = [&](int jt, auto par_tag, auto masked_tag, auto next_tag) __attribute__((always_inline)) {
+    // One key tile jt (buffer parity PAR): its scores are in sacc[PAR]; K(jn)
+    // and V(jt) are in LDS, where jn and jn2 are the next two tiles visited.
+    // MASKED: the tile crosses the edge of some row's visible band.  NEXT: a
+    // tile jn exists.
+    auto step = [&](int jt, int jn, int jn2, auto par_tag, auto masked_tag, auto next_tag)
+                    __attribute__((always_inline)) {
         constexpr int PAR = decltype(par_tag)::value;
         constexpr bool MASKED = decltype(masked_tag)::value;
         constexpr bool NEXT = decltype(next_tag)::value;
         const int k0 = jt * kBK;
-        // Every wave has finished tile jt-1 (the K(jt) and V(jt-1) buffers
-        // are free) and the DMA of K(jt+1), V(jt) has landed.
+        // Every wave has finished the previous tile (its K(jt) and V buffers
+        // are free) and the DMA of K(jn), V(jt) has landed.
         __syncthreads();
         if (NEXT) {
-            if (jt + 2 < tr.end) dma_tile<D, kBK>(Kh, k0 + 2 * kBK, nk, Kb + PAR * TB, w, lane, goff);
-            dma_tile<D, kBK>(Vh, k0 + kBK, nk, Vb + (1 - PAR) * TB, w, lane, goff);
+            if (jn2 < tr.end) dma_tile<D, kBK>(Kh, jn2 * kBK, nk, Kb + PAR * TB, w, lane, goff);
+            dma_tile<D, kBK>(Vh, jn * kBK, nk, Vb + (1 - PAR) * TB, w, lane, goff);
         }
         float mc[QB];
 #pragma unroll
@@ -191,11 +224,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                         if (key < klo || key > khi) s[kb][e] = kNegInf;
                     }
             }
-            float mx = s[0][0];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
+            float mx = max32(s[0], s[1]);
             mx = max_with_other_half(mx);
             // Raise m (and rescale) only when the maximum grew by more than 2^8.
             const bool grow = mx > m[qb] && (m[qb] == kNegInf || (mx - m[qb]) * c > kLazy);
@@ -225,9 +254,13 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                 for (int e = 0; e < 16; ++e) {
                     float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], c, -mc[qb]));
                     if constexpr (MASKED) pe = sv[e] == kNegInf ? 0.f : pe;
-                    l[qb] += pe;  // the running sum adds the fp32 exponentials
                     p[e] = pe;
                 }
+                // the running sum adds the fp32 exponentials (four short chains)
+                float l4[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) l4[i] = (p[i] + p[i + 4]) + (p[i + 8] + p[i + 12]);
+                l[qb] += (l4[0] + l4[1]) + (l4[2] + l4[3]);
                 pack_acc_as_b<T>(p, pf[qb][kb][0], pf[qb][kb][1]);
             }
         // O^T += V^T P^T: each V^T fragment read from LDS feeds QB MFMAs
@@ -245,31 +278,50 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         wait_dma();
     };
 
-    // Tiles [a, b) all of one kind (masked or not), none of them the last.
-    auto run = [&](int a, int b, auto masked_tag) __attribute__((always_inline)) {
-        int jt = a;
-        if (jt < b && (jt & 1)) {
-            step(jt, Flag<1>{}, masked_tag, Flag<true>{});
-            ++jt;
+    if constexpr (!BS) {
+        // Tiles [a, b) all of one kind (masked or not), none of them the last.
+        auto run = [&](int a, int b, auto masked_tag) __attribute__((always_inline)) {
+            int jt = a;
+            if (jt < b && (jt & 1)) {
+                step(jt, jt + 1, jt + 2, Flag<1>{}, masked_tag, Flag<true>{});
+                ++jt;
+            }
+            for (; jt + 1 < b; jt += 2) {
+                step(jt, jt + 1, jt + 2, Flag<0>{}, masked_tag, Flag<true>{});
+                step(jt + 1, jt + 2, jt + 3, Flag<1>{}, masked_tag, Flag<true>{});
+            }
+            if (jt < b) step(jt, jt + 1, jt + 2, Flag<0>{}, masked_tag, Flag<true>{});
+        };
+        if (tr.end > tr.first) {
+            const int last = tr.end - 1;
+            run(tr.first, min(tr.full_first, last), Flag<true>{});
+            run(tr.full_first, min(tr.full_end, last), Flag<false>{});
+            run(max(tr.full_end, tr.full_first), last, Flag<true>{});
+            const bool last_masked = last < tr.full_first || last >= tr.full_end;
+            if (last & 1) {
+                if (last_masked) step(last, tr.end, tr.end, Flag<1>{}, Flag<true>{}, Flag<false>{});
+                else step(last, tr.end, tr.end, Flag<1>{}, Flag<false>{}, Flag<false>{});
+            } else {
+                if (last_masked) step(last, tr.end, tr.end, Flag<0>{}, Flag<true>{}, Flag<false>{});
+                else step(last, tr.end, tr.end, Flag<0>{}, Flag<false>{}, Flag<false>{});
+            }
         }
-        for (; jt + 1 < b; jt += 2) {
-            step(jt, Flag<0>{}, masked_tag, Flag<true>{});
-            step(jt + 1, Flag<1>{}, masked_tag, Flag<true>{});
-        }
-        if (jt < b) step(jt, Flag<0>{}, masked_tag, Flag<true>{});
-    };
-    if (tr.end > tr.first) {
-        const int last = tr.end - 1;
-        run(tr.first, min(tr.full_first, last), Flag<true>{});
-        run(tr.full_first, min(tr.full_end, last), Flag<false>{});
-        run(max(tr.full_end, tr.full_first), last, Flag<true>{});
-        const bool last_masked = last < tr.full_first || last >= tr.full_end;
-        if (last & 1) {
-            if (last_masked) step(last, Flag<1>{}, Flag<true>{}, Flag<false>{});
-            else step(last, Flag<1>{}, Flag<false>{}, Flag<false>{});
-        } else {
-            if (last_masked) step(last, Flag<0>{}, Flag<true>{}, Flag<false>{});
-            else step(last, Flag<0>{}, Flag<false>{}, Flag<false>{});
+    } else {
+        // Walk the active tiles, each with the per-element test (it is exact
+        // for every tile, and one step body per buffer parity keeps the loop
+        // within the register budget).
+        auto visit = [&](int jt, int jn, int jn2, auto par_tag) __attribute__((always_inline)) {
+            if (jn < tr.end) step(jt, jn, jn2, par_tag, Flag<true>{}, Flag<true>{});
+            else step(jt, jn, jn2, par_tag, Flag<true>{}, Flag<false>{});
+        };
+        int jt = j0, jn = j1, par = 0;
+        while (jt < tr.end) {
+            const int jn2 = jn < tr.end ? next_tile(jn) : tr.end;
+            if (par) visit(jt, jn, jn2, Flag<1>{});
+            else visit(jt, jn, jn2, Flag<0>{});
+            jt = jn;
+            jn = jn2;
+            par ^= 1;
         }
     }
     __syncthreads();  // every wave is done with the tile buffers
@@ -301,30 +353,31 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     }
 }
 
-template <class T, int D>
+template <class T, int D, bool BS>
 hipError_t launch(const FwdParams& p) {
-    constexpr int QB = ATTN_FWD_QB, BQ = kWaves * 32 * QB;
+    constexpr int QB = BS ? 1 : ATTN_FWD_QB, BQ = kWaves * 32 * QB;
     const int ntq = (p.max_nq + BQ - 1) / BQ;
     const int64_t nseq = (int64_t)p.L.B * p.L.H;
     const int64_t blocks = nseq * ntq;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D, QB>), dim3((unsigned)blocks), dim3(kThreads), 0,
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, QB, BS>), dim3((unsigned)blocks), dim3(kThreads), 0,
                        (hipStream_t)p.stream, (const uint16_t*)p.q, (const uint16_t*)p.k,
                        (const uint16_t*)p.v, (uint16_t*)p.o, p.lse, p.L, ntq, p.scale,
                        p.scale * kLog2e);
     return hipGetLastError();
 }
 
-template <class T>
+template <class T, bool BS>
 hipError_t launch_d(const FwdParams& p) {
-    return p.d == 64 ? launch<T, 64>(p) : launch<T, 128>(p);
+    return p.d == 64 ? launch<T, 64, BS>(p) : launch<T, 128, BS>(p);
 }
 
 }  // namespace
 
 hipError_t launch_fwd(const FwdParams& p) {
-    return p.dtype == kDtypeBF16 ? launch_d<BF16>(p) : launch_d<F16>(p);
+    if (p.L.bmask) return p.dtype == kDtypeBF16 ? launch_d<BF16, true>(p) : launch_d<F16, true>(p);
+    return p.dtype == kDtypeBF16 ? launch_d<BF16, false>(p) : launch_d<F16, false>(p);
 }
 
 }  // namespace attn

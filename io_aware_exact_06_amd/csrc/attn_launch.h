@@ -24,6 +24,13 @@ constexpr int kDtypeBF16 = 1;
 // pos = i + nk - nq (rows aligned to the end of the keys).  Key j is visible
 // iff (wl < 0 or j >= pos - wl) and (wr < 0 or j <= pos + wr); a causal call
 // is wr = 0.
+//
+// Block mask (dense calls only; bmask == nullptr: none): bytes
+// [bm_heads, bm_nb, bm_nb], bm_nb = ceil(N / kMaskBlock); key j is visible
+// from row i of sequence s = b*H + h only if bmask[m][i / 128][j / 128] != 0
+// with m = 0 (bm_heads == 1), h (bm_heads == H) or s (bm_heads == B*H).
+constexpr int kMaskBlock = 128;
+
 struct SeqLayout {
     int mode;
     int B, H, N;
@@ -31,6 +38,8 @@ struct SeqLayout {
     const int* cu_k;
     int total_q, total_k;
     int wl, wr;
+    const uint8_t* bmask;
+    int bm_heads, bm_nb;
 };
 
 struct FwdParams {

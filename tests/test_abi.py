@@ -162,3 +162,24 @@ def test_fwd_unfused_validation():
     assert call(ws=A + 0x500004) == 4
     assert call(o=A + 0x200000) == 5
     assert call(ws=A + 0x300000) == 6
+
+
+def test_blocksparse_validation():
+    B, H, N, d = 1, 2, 300, 64          # nb = 3 blocks of 128
+    nb = 3
+    q, k, v, o, lse, bm = A, A + 0x100000, A + 0x200000, A + 0x300000, A + 0x400000, A + 0x500000
+    f = lambda **kw: attn.attn_fwd_blocksparse(kw.get("q", q), k, v, kw.get("o", o), lse, B, H, kw.get("N", N), d,
+                                               kw.get("bm", bm), kw.get("mh", 1), 1, 0.125, 1, None)
+    assert f(bm=None) == 1                  # a block mask is required
+    assert f(mh=3) == 2 and f(mh=0) == 2    # mask_heads must be 1, H or B*H
+    assert f(o=bm - 16) == 5                # the output overlaps the mask ([1, 3, 3] bytes)
+    assert f(N=0, bm=None) == 0             # empty problems do nothing
+    assert f(mh=2, o=bm + 16) == 5          # [2, 3, 3] bytes reach the output at byte 16
+    assert f(mh=1, q=0) == 1
+    ws = A + 0x600000
+    need = attn.attn_bwd_workspace_bytes(B, H, N, d)
+    g = lambda **kw: attn.attn_bwd_blocksparse(q, k, v, o, A + 0x700000, lse, kw.get("dq", A + 0x800000),
+                                               A + 0x900000, A + 0xa00000, B, H, N, d, kw.get("bm", bm),
+                                               kw.get("mh", 2), 0, 0.125, 1, ws, need, None)
+    assert g(bm=None) == 1 and g(mh=5) == 2
+    assert g(dq=bm - 16) == 5               # a gradient overlaps the mask
