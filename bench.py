@@ -5,13 +5,15 @@ the forward (O and lse) and the recompute backward (dQ, dK, dV) of
 B=1, H=32, N=8192, d=128, causal, bf16 attention with inputs resident in HBM.
 
     python bench.py [--steps K] [--warmup W] [--passes fwd|fwdbwd] [--no-cpu-baseline]
-                    [--workload headline|window512|varlen|io] [--n N]
+                    [--workload headline|window512|varlen|blocksparse|io] [--n N]
 
 The default (headline) workload is the one above.  `window512` runs the same
 shape with a causal sliding window of 512 keys (local attention, through the
 packed-sequence entry points with one sequence); `varlen` runs a packed batch
 of 16 causal sequences of seeded lengths between 256 and 4096 (32 heads,
-d=128, bf16).  `io` times the fused forward against the unfused three-pass
+d=128, bf16).  `blocksparse` runs the headline shape with a seeded per-head
+mask of 128 x 128 blocks, half of them active (attn_fwd_blocksparse /
+attn_bwd_blocksparse).  `io` times the fused forward against the unfused three-pass
 forward (B=1, H=8, N=--n, d=128, bf16, causal) and runs one plain 1 GiB device
 copy; run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE it gives each kernel's
 memory traffic, the copy serving as the counters' calibration.  Prints one
@@ -193,6 +195,76 @@ def bench_packed(args, workload):
     print(json.dumps(out), flush=True)
 
 
+def bench_blocksparse(args):
+    """Headline shape with a per-head 50% random block mask (seed 2025), causal."""
+    import numpy as np
+    import torch
+
+    from io_aware_exact_06_amd import attn
+    from io_aware_exact_06_amd.inputs import default_scale, make_inputs
+    B, H, N, d = 1, 32, 8192, 128
+    nb = N // attn.MASK_BLOCK
+    rng = np.random.default_rng(2025)
+    mask = (rng.random((H, nb, nb)) < 0.5).astype(np.uint8)
+    mask[:, np.arange(nb), np.arange(nb)] = 1  # every row keeps its diagonal block
+    # visible (query, key) pairs: active blocks, causal inside the diagonal blocks
+    tri = attn.MASK_BLOCK * (attn.MASK_BLOCK + 1) // 2
+    full = attn.MASK_BLOCK * attn.MASK_BLOCK
+    low = np.tril(np.ones((nb, nb), bool), -1)
+    pairs = int(sum(mask[h][low].sum() * full + np.trace(mask[h]) * tri for h in range(H)))
+    inp = make_inputs(B, H, N, d, "bf16", 1003, with_dout=True)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "dout"))
+    m = torch.from_numpy(mask).to(dev)
+    scale = default_scale(d)
+    bwd = "bwd" in args.passes
+
+    def run(ev=None):
+        if ev is not None:
+            ev[0].record()
+        o, lse = attn.fwd_blocksparse(q, k, v, m, True, scale)
+        if ev is not None:
+            ev[1].record()
+        if bwd:
+            attn.bwd_blocksparse(q, k, v, o, do, lse, m, True, scale)
+            if ev is not None:
+                ev[2].record()
+        return o
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        o = run(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps if bwd else 0.0
+    f_tf = 4.0 * d * pairs / (fwd_ms * 1e-3) / 1e12
+    b_tf = 10.0 * d * pairs / (bwd_ms * 1e-3) / 1e12 if bwd else None
+    ms_step = wall * 1e3 / args.steps
+    out = {
+        "metric": METRIC, "value": round((4.0 + (10.0 if bwd else 0.0)) * d * pairs / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic: iid N(0,1) fp32 rounded to bf16, seed 1003; mask seed 2025",
+        "config": {"workload": "fwdbwd_B1_H32_N8192_d128_bf16_causal_blocksparse50", "B": B, "H": H, "N": N,
+                   "d": d, "causal": True, "mask_block": attn.MASK_BLOCK,
+                   "active_blocks": int(mask.sum()), "visible_pairs": pairs, "passes": args.passes},
+        "fwd": {"avg_ms": round(fwd_ms, 4), "tflops": round(f_tf, 2), "pct_peak": round(100 * f_tf / PEAK_BF16_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(b_tf if bwd else f_tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round((b_tf if bwd else f_tf) / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "attn_bwd_blocksparse pass" if bwd else "attn_fwd_kernel (block mask)"},
+        "outputs_finite": bool(torch.isfinite(o).all()),
+    }
+    if bwd:
+        out["bwd"] = {"avg_ms": round(bwd_ms, 4), "tflops": round(b_tf, 2),
+                      "pct_peak": round(100 * b_tf / PEAK_BF16_TFLOPS, 2)}
+    print(json.dumps(out), flush=True)
+
+
 def bench_io(args):
     """Fused vs unfused forward at one sequence length, plus a calibration copy."""
     import torch
@@ -237,7 +309,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--passes", choices=["fwd", "fwdbwd"], default="fwdbwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=["headline", "window512", "varlen", "io"], default="headline")
+    ap.add_argument("--workload", choices=["headline", "window512", "varlen", "blocksparse", "io"],
+                    default="headline")
     ap.add_argument("--n", type=int, default=4096, help="sequence length of the io workload")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -255,6 +328,9 @@ def main():
         __graft_entry__.build()
     if args.workload == "io":
         bench_io(args)
+        return
+    if args.workload == "blocksparse":
+        bench_blocksparse(args)
         return
     if args.workload != "headline":
         bench_packed(args, args.workload)

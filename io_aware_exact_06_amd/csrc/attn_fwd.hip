@@ -71,7 +71,7 @@ __device__ inline float max32(const f32x16& a, const f32x16& b) {
 
 template <class T, int D, int QB, bool BS>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(QB == 1 && !BS ? 2 : 1, QB == 1 && !BS ? 2 : 1)))
+                          amdgpu_waves_per_eu(QB == 1 ? 2 : 1, QB == 1 ? 2 : 1)))
 void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                      float* __restrict__ LSE, SeqLayout L, int ntq, float scale, float c) {
@@ -173,7 +173,11 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     if (BS)
         while (j0 < tr.end && !bmrow[j0 >> 1]) ++j0;
     const int j1 = j0 < tr.end ? next_tile(j0) : tr.end;
-    const int p0 = BS ? 0 : (j0 & 1);  // buffer parity of the first tile
+    // Buffer parity is the tile index parity.  With a block mask the visited
+    // tiles still alternate in parity: an active block is the tile pair
+    // (2b, 2b+1), so the walk only ever jumps from an odd tile to an even one
+    // (clipping to [tr.first, tr.end) removes tiles only at its two ends).
+    const int p0 = j0 & 1;
 
     // Prologue: tiles j0 (K, V) and j1 (K) in flight, then the scores of j0.
     if (j0 < tr.end) {
@@ -307,21 +311,32 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             }
         }
     } else {
-        // Walk the active tiles, each with the per-element test (it is exact
-        // for every tile, and one step body per buffer parity keeps the loop
-        // within the register budget).
-        auto visit = [&](int jt, int jn, int jn2, auto par_tag) __attribute__((always_inline)) {
-            if (jn < tr.end) step(jt, jn, jn2, par_tag, Flag<true>{}, Flag<true>{});
-            else step(jt, jn, jn2, par_tag, Flag<true>{}, Flag<false>{});
-        };
-        int jt = j0, jn = j1, par = 0;
-        while (jt < tr.end) {
-            const int jn2 = jn < tr.end ? next_tile(jn) : tr.end;
-            if (par) visit(jt, jn, jn2, Flag<1>{});
-            else visit(jt, jn, jn2, Flag<0>{});
+        // Walk the active tiles, each with the per-element test (exact for
+        // every tile); two steps per iteration, of fixed parities, as in the
+        // dense loop, and the last tile after the loop.
+        int jt = j0, jn = j1;
+        if (jt < tr.end && jn < tr.end && (jt & 1)) {
+            const int jn2 = next_tile(jn);
+            step(jt, jn, jn2, Flag<1>{}, Flag<true>{}, Flag<true>{});
             jt = jn;
             jn = jn2;
-            par ^= 1;
+        }
+        while (jn < tr.end) {  // jt is even and has a successor
+            const int jn2 = next_tile(jn);
+            step(jt, jn, jn2, Flag<0>{}, Flag<true>{}, Flag<true>{});
+            if (jn2 >= tr.end) {
+                jt = jn;
+                jn = jn2;
+                break;
+            }
+            const int jn3 = next_tile(jn2);
+            step(jn, jn2, jn3, Flag<1>{}, Flag<true>{}, Flag<true>{});
+            jt = jn2;
+            jn = jn3;
+        }
+        if (jt < tr.end) {  // the last tile
+            if (jt & 1) step(jt, tr.end, tr.end, Flag<1>{}, Flag<true>{}, Flag<false>{});
+            else step(jt, tr.end, tr.end, Flag<0>{}, Flag<true>{}, Flag<false>{});
         }
     }
     __syncthreads();  // every wave is done with the tile buffers
