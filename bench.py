@@ -50,9 +50,9 @@ METRIC = "fused attention fwd/bwd TFLOP/s and % MFMA peak, N=8192 d=128 causal b
 # other sources the traffic is reported as null.
 TRAFFIC_SOURCES = ("attn_device.h", "attn_launch.h", "attn_fwd.hip", "attn_bwd.hip")
 TRAFFIC = {
-    "sha256": "406773809a5f85864da4a0310f662a41905a45d75594e41a356ab9c889b69bcd",
-    "fwd": 288819200,             # attn_fwd_kernel: fetch 2 x 107745.0 KiB + write 66560.0 KiB
-    "bwd": 479659622 + 409856819,  # attn_bwd_dq_kernel (2 x 199911.5 + 68594.6 KiB) + attn_bwd_dkdv_kernel (2 x 134589.4 + 131072.0 KiB)
+    "sha256": "22472d708c67218a4ea735a4b857454557d86608ce88631719687bad824f992f",
+    "fwd": 297139904,             # attn_fwd_kernel: fetch 2 x 111807.8 KiB + write 66560.0 KiB
+    "bwd": 500053152 + 424499264,  # attn_bwd_dq_kernel (2 x 210886.6 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 141739.0 + 131072.0 KiB)
 }
 
 
