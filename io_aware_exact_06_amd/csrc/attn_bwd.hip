@@ -27,6 +27,10 @@
 // The second kernel recomputes S and dP, so the backward performs seven
 // d-deep products per unmasked pair instead of five; it buys freedom from
 // atomics and a deterministic result.
+//
+// Both kernels stream their tiles through LDS by DMA (double-buffered, in the
+// swizzled layout of DmaTile) and, with a block mask, visit only the tiles of
+// active (query block, key block) pairs.
 
 #include "attn_device.h"
 #include "attn_launch.h"

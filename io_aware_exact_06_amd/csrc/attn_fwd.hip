@@ -1,9 +1,10 @@
 // attn_fwd.hip -- fused exact-attention forward for gfx950.
 //
 // One work group owns 128 query rows of one sequence (of one head): four
-// waves of 32 rows (QB blocks of 32 rows per wave in general).  Keys and values stream through LDS in tiles of 64 rows,
-// double-buffered and loaded by the DMA path (global_load_lds: global memory
-// straight into LDS, no registers); each wave keeps, for its rows, the
+// waves of 32 rows (QB blocks of 32 rows per wave in general).  Keys and
+// values stream through LDS in tiles of 64 rows, double-buffered and loaded
+// by the DMA path (global_load_lds: global memory straight into LDS, no
+// registers); each wave keeps, for its rows, the
 // running maximum m, the running sum l and the partial output in registers:
 // the online softmax of the hotdry blog's section "3. 在线softmax算法"
 // (initialise m = -inf and l = 0; for every key block raise the maximum,
@@ -33,7 +34,9 @@
 //
 // Causal and window masking (snabindia chapter 1: the causal call skips the
 // upper triangle): key tiles no row of the group sees are never loaded; only
-// tiles at the edge of the visible band are masked element by element.
+// tiles at the edge of the visible band are masked element by element.  With
+// a block mask (the same page's skipping of all-zero blocks, chapter 1 and
+// section 3.1) the group visits only the key tiles of its active blocks.
 
 #include "attn_device.h"
 #include "attn_launch.h"
