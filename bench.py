@@ -46,23 +46,33 @@ METRIC = "fused attention fwd/bwd TFLOP/s and % MFMA peak, N=8192 d=128 causal b
 # --steps 3 --warmup 1`, scaled by what the same counters read for a plain 1 GiB
 # device copy (FETCH_SIZE reads half the copied bytes: factor 2.0; WRITE_SIZE
 # reads them exactly: factor 1.0).  The figures hold only for the kernel
-# sources they were taken on, whose SHA-256 is stored beside them; for any
-# other sources the traffic is reported as null.
+# code they were taken on, whose digest (kernel_code_digest) is stored beside
+# them; for any other code the traffic is reported as null.
 TRAFFIC_SOURCES = ("attn_device.h", "attn_launch.h", "attn_fwd.hip", "attn_bwd.hip")
 TRAFFIC = {
-    "sha256": "22472d708c67218a4ea735a4b857454557d86608ce88631719687bad824f992f",
+    "sha256": "a5ba07cea8d7c99a24da8abfc65db8ccf1056f4b0685568ea6a93961caa3fd40",
     "fwd": 297139904,             # attn_fwd_kernel: fetch 2 x 111807.8 KiB + write 66560.0 KiB
     "bwd": 500053152 + 424499264,  # attn_bwd_dq_kernel (2 x 210886.6 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 141739.0 + 131072.0 KiB)
 }
 
 
-def measured_traffic(which):
+def kernel_code_digest():
+    """SHA-256 of the kernel sources with comments and whitespace removed: a
+    change to the code changes it, a change to a comment does not."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in TRAFFIC_SOURCES:
-        with open(os.path.join(ROOT, "io_aware_exact_06_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return TRAFFIC[which] if h.hexdigest() == TRAFFIC["sha256"] else None
+        with open(os.path.join(ROOT, "io_aware_exact_06_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()
+
+
+def measured_traffic(which):
+    return TRAFFIC[which] if kernel_code_digest() == TRAFFIC["sha256"] else None
 
 
 def flops(w, passes):

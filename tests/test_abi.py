@@ -183,3 +183,20 @@ def test_blocksparse_validation():
                                                kw.get("mh", 2), 0, 0.125, 1, ws, need, None)
     assert g(bm=None) == 1 and g(mh=5) == 2
     assert g(dq=bm - 16) == 5               # a gradient overlaps the mask
+
+
+def test_bench_traffic_gate():
+    """bench.py reports the stored HBM traffic only for the kernel code it was
+    measured on (comments aside)."""
+    import sys
+    sys.path.insert(0, ROOT)
+    import bench
+    digest = bench.kernel_code_digest()
+    saved = dict(bench.TRAFFIC)
+    try:
+        bench.TRAFFIC["sha256"] = digest
+        assert bench.measured_traffic("fwd") == saved["fwd"]
+        bench.TRAFFIC["sha256"] = "0" * 64
+        assert bench.measured_traffic("fwd") is None and bench.measured_traffic("bwd") is None
+    finally:
+        bench.TRAFFIC.update(saved)
