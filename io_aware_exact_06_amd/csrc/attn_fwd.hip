@@ -248,7 +248,11 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             mc[qb] = (m[qb] == kNegInf) ? 0.f : m[qb] * c;
         }
         // Scores of the next tile on the matrix cores while P of this tile
-        // is formed on the vector unit.
+        // is formed on the vector unit.  The wave issues this MFMA-heavy part
+        // at raised priority, so that the other wave on the SIMD (in its
+        // maximum and rescale code, or at the barrier) fills the gaps rather
+        // than competing for issue slots (measured: 4-5% faster at d = 128).
+        prio_mfma();
         if (NEXT) scores(Flag<1 - PAR>{});
         u32x4 pf[QB][2][2];
 #pragma unroll
@@ -282,6 +286,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32<T>(a, pf[qb][kb][t], oacc[qb][db]);
                 }
+        prio_normal();
         wait_dma();
     };
 
