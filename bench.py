@@ -50,9 +50,9 @@ METRIC = "fused attention fwd/bwd TFLOP/s and % MFMA peak, N=8192 d=128 causal b
 # them; for any other code the traffic is reported as null.
 TRAFFIC_SOURCES = ("attn_device.h", "attn_launch.h", "attn_fwd.hip", "attn_bwd.hip")
 TRAFFIC = {
-    "sha256": "a5ba07cea8d7c99a24da8abfc65db8ccf1056f4b0685568ea6a93961caa3fd40",
-    "fwd": 297139904,             # attn_fwd_kernel: fetch 2 x 111807.8 KiB + write 66560.0 KiB
-    "bwd": 500053152 + 424499264,  # attn_bwd_dq_kernel (2 x 210886.6 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 141739.0 + 131072.0 KiB)
+    "sha256": "aa54eacec0f9f8d85995837cac70ade033e3899e1678f8cfa1fef3538f78ae7e",
+    "fwd": 289471898,             # attn_fwd_kernel: fetch 2 x 108063.7 KiB + write 66560.0 KiB
+    "bwd": 501436211 + 424085504,  # attn_bwd_dq_kernel (2 x 211561.9 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 141537.0 + 131072.0 KiB)
 }
 
 
