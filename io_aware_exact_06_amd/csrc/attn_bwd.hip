@@ -28,9 +28,11 @@
 // d-deep products per unmasked pair instead of five; it buys freedom from
 // atomics and a deterministic result.
 //
-// Both kernels stream their tiles through LDS by DMA (double-buffered, in the
-// swizzled layout of DmaTile) and, with a block mask, visit only the tiles of
-// active (query block, key block) pairs.
+// Both kernels stream their tiles through LDS by DMA (in the swizzled layout
+// of DmaTile: double-buffered in the first, a ring of three in the second,
+// which overlaps the vector work of one query block with the matrix products
+// of the block before) and, with a block mask, visit only the tiles of active
+// (query block, key block) pairs.
 
 #include "attn_device.h"
 #include "attn_launch.h"
@@ -269,16 +271,23 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 
 // ============================================================================
 // dK and dV: one work group per (sequence, 128 key rows), 4 waves x 32 keys.
-// Q and dO tiles of 64 rows stream through LDS by DMA (double-buffered).
-// At d = 128 the resident K, V fragments and both accumulators need more than
-// the 256 registers of a two-waves-per-SIMD budget, so this kernel runs one
-// wave per SIMD there (forcing two spills heavily); at d = 64 it runs two.
+// Q and dO tiles of 64 rows stream through LDS by DMA, in a ring of three
+// buffers.
+//
+// Software pipeline (per wave, over the 32-row query blocks b of the visited
+// tiles): while the vector unit forms P and dS of block b, the matrix cores
+// run the dV, dK products of block b - 1.  With one wave per SIMD (d = 128)
+// no other wave could fill the matrix cores while this one does vector work,
+// so the overlap has to come from independent instructions of the same wave.
+// Block b - 1 may lie in the previous tile, which therefore stays in LDS
+// while the tile after the current one is loaded: a ring of three.
 // ============================================================================
 constexpr int kK_BK = 128;
 constexpr int kK_BQ = 64;
+constexpr int kK_NBUF = 3;
 
 template <class T, int D, bool BS>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(D == 64 ? 2 : 1, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 2)))
 void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                           const float* __restrict__ LSE, const float* __restrict__ Delta,
@@ -286,13 +295,11 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
                           float scale, float c) {
     using DT = DmaTile<D, kK_BQ>;
     constexpr int STR = LdsStride<D>::value;  // row stride of the output staging
-    constexpr int KS = D / 16, DB = D / 32, QB = kK_BQ / 32;
+    constexpr int KS = D / 16, DB = D / 32;
     constexpr int TB = DT::ELEMS;
-    constexpr int SMEM = (kK_BK * STR > 4 * TB) ? kK_BK * STR : 4 * TB;
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM];
-    __shared__ __attribute__((aligned(16))) float stats[2][2][kK_BQ];  // [buffer][lse*log2e, D][row]
-    uint16_t* const Qs = smem;            // Q tiles: buffers 0, 1
-    uint16_t* const dOs = smem + 2 * TB;  // dO tiles: buffers 0, 1
+    constexpr int SMEM = (kK_BK * STR > 2 * kK_NBUF * TB) ? kK_BK * STR : 2 * kK_NBUF * TB;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM];  // buffer b: Q tile 2b, dO tile 2b + 1
+    __shared__ __attribute__((aligned(16))) float stats[kK_NBUF][2][kK_BQ];  // [buffer][lse*log2e, D][row]
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -307,8 +314,7 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     const uint16_t *Kh = K + sq.krow0 * D, *Vh = V + sq.krow0 * D;
     const float* lseh = LSE + sq.qrow0;
     const float* Dh = Delta + sq.qrow0;
-    const int wk0 = k0 + 32 * w;
-    const int krow = wk0 + n32;
+    const int krow = k0 + 32 * w + n32;
 
     // Resident K and V fragments (B operands of S = Q K^T and dP = dO V^T).
     // Keys past the end read row nk-1; their dK and dV are never written.
@@ -327,20 +333,6 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     const int klast = min(k0 + kK_BK, nk) - 1;
     const TileRange tr = tile_range(sq.row_lo(k0), sq.row_hi(klast), sq.row_lo(klast), sq.row_hi(k0), nq, kK_BQ);
     const uint32_t goff = DT::lane_goff(lane);
-    float st_l = kPosInf, st_d = 0.f;
-    auto load_stats = [&](int r0) {
-        if (tid < kK_BQ) {
-            const int r = r0 + tid;
-            st_l = r < nq ? lseh[r] * kLog2e : kPosInf;  // rows past the end get P = 0
-            st_d = r < nq ? Dh[r] : 0.f;
-        }
-    };
-    auto store_stats = [&](int sb) {
-        if (tid < kK_BQ) {
-            stats[sb][0][tid] = st_l;
-            stats[sb][1][tid] = st_d;
-        }
-    };
     // With a block mask only the query tiles of active (query block, key
     // block) pairs are visited: a 64-row tile lies in mask block t / 2, and
     // this group's 128 keys are key block kt (the mask column is read with
@@ -353,18 +345,27 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
             while (t < tr.end && !bmcol[(size_t)(t >> 1) * sq.nb]) ++t;
         return t;
     };
-    int i0 = tr.first;
-    if (BS)
-        while (i0 < tr.end && !bmcol[(size_t)(i0 >> 1) * sq.nb]) ++i0;
-    if (i0 < tr.end) {
-        const int r0 = i0 * kK_BQ;
-        dma_tile<D, kK_BQ>(Qh, r0, nq, Qs, w, lane, goff);
-        dma_tile<D, kK_BQ>(dOh, r0, nq, dOs, w, lane, goff);
-        load_stats(r0);
-        store_stats(0);
-    }
-    wait_dma();  // unconditional (see the dq kernel)
-    __syncthreads();
+
+    // Tile `it` into ring buffer b: Q and dO by DMA, the row statistics into
+    // registers (stored to LDS later, once the buffer's previous statistics
+    // are no longer read).
+    float st_l = kPosInf, st_d = 0.f;
+    auto fetch = [&](int it, int b) __attribute__((always_inline)) {
+        const int r0 = it * kK_BQ;
+        dma_tile<D, kK_BQ>(Qh, r0, nq, smem + 2 * b * TB, w, lane, goff);
+        dma_tile<D, kK_BQ>(dOh, r0, nq, smem + (2 * b + 1) * TB, w, lane, goff);
+        if (tid < kK_BQ) {
+            const int r = r0 + tid;
+            st_l = r < nq ? lseh[r] * kLog2e : kPosInf;  // rows past the end get P = 0
+            st_d = r < nq ? Dh[r] : 0.f;
+        }
+    };
+    auto store_stats = [&](int b) __attribute__((always_inline)) {
+        if (tid < kK_BQ) {
+            stats[b][0][tid] = st_l;
+            stats[b][1][tid] = st_d;
+        }
+    };
 
     f32x16 dkacc[DB], dvacc[DB];
 #pragma unroll
@@ -377,97 +378,185 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     const uint32_t fo[2] = {DT::frag_lane(lane, 0), DT::frag_lane(lane, 1)};
     const uint32_t to0 = DT::tr_lane(lane, 0), to1 = DT::tr_lane(lane, 1);
 
-    // Query tile it in buffer sb; in is the next tile visited.
-    auto step = [&](int it, int in, int sb, auto masked_tag) __attribute__((always_inline)) {
-        constexpr bool MASKED = decltype(masked_tag)::value;
-        const int qq0 = it * kK_BQ;
-        const bool more = in < tr.end;
-        // the other buffers held the previous tile, which every wave has finished
-        if (more) {
-            dma_tile<D, kK_BQ>(Qh, in * kK_BQ, nq, Qs + (1 - sb) * TB, w, lane, goff);
-            dma_tile<D, kK_BQ>(dOh, in * kK_BQ, nq, dOs + (1 - sb) * TB, w, lane, goff);
-            load_stats(in * kK_BQ);
+    // ---- the parts of a block (qb: the block's index in its tile).  Each
+    // issues all LDS operand reads of its MFMAs first, then runs as a fixed
+    // sequence of steps, one MFMA per step; a scheduling barrier after every
+    // step keeps the compiler from regrouping the vector work (measured: one
+    // element's vector work per MFMA step is fastest at d = 128).
+    // S = Q K^T and dP = dO V^T of block qb of the tile in buffer b.
+    // Operand i: k-step i / 2 of S (i even, Q fragment) or dP (i odd, dO).
+    auto part_a = [&](int b, auto qb_tag, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
+        constexpr int QBI = decltype(qb_tag)::value;
+        const char* qt_ = (const char*)(smem + 2 * b * TB);
+        const char* ot_ = (const char*)(smem + (2 * b + 1) * TB);
+        auto rd = [&](int i) __attribute__((always_inline)) {
+            return *(const u32x4*)(((i & 1) ? ot_ : qt_) + fo[(i >> 1) & 1] + DT::frag_blk(QBI, i >> 1));
+        };
+        u32x4 fa[2 * KS];
+#pragma unroll
+        for (int i = 0; i < 2 * KS; ++i) fa[i] = rd(i);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            s[e] = 0.f;
+            dp[e] = 0.f;
         }
-        const char* qt_ = (const char*)(Qs + sb * TB);
-        const char* ot_ = (const char*)(dOs + sb * TB);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            const int qb0 = qq0 + 32 * qb;  // first query row of this 32-row block
-            // skip a block none of whose rows sees a key of this wave
-            if (MASKED && (qb0 + 31 < sq.row_lo(wk0) || qb0 > sq.row_hi(wk0 + 31))) continue;
-            // ---- S = Q K^T and dP = dO V^T
-            f32x16 s, dp;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                s[e] = 0.f;
-                dp[e] = 0.f;
-            }
-            prio_mfma();
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int o = DT::frag_blk(qb, ks);
-                s = mfma32<T>(*(const u32x4*)(qt_ + fo[ks & 1] + o), kf[ks], s);
-                dp = mfma32<T>(*(const u32x4*)(ot_ + fo[ks & 1] + o), vf[ks], dp);
-            }
-            sched_reads_ahead<4, 2 * KS, 1>();
-            prio_normal();
-            // Row statistics of the 16 query rows this lane holds: rows 8g + 4h + (0..3).
-            f32x16 ls, dd;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4 l4 = *(const f32x4*)(&stats[sb][0][32 * qb + 8 * g + 4 * h]);
-                const f32x4 d4 = *(const f32x4*)(&stats[sb][1][32 * qb + 8 * g + 4 * h]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    ls[4 * g + i] = l4[i];
-                    dd[4 * g + i] = d4[i];
-                }
-            }
-            // ---- P = exp(scale s - lse), dS = P o (dP - D)
-            f32x16 p, ds;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -ls[e]));
-                if constexpr (MASKED) {
-                    if (!sq.visible(qb0 + 8 * (e >> 2) + 4 * h + (e & 3), krow)) pe = 0.f;
-                }
-                p[e] = pe;
-                ds[e] = pe * (dp[e] - dd[e]);
-            }
-            u32x4 bp[2], bds[2];
-            pack_acc_as_b<T>(p, bp[0], bp[1]);
-            pack_acc_as_b<T>(ds, bds[0], bds[1]);
-            // ---- dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T read transposed)
-            prio_mfma();
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int o = DT::tr_blk(2 * qb + t, db);
-                    dvacc[db] = mfma32<T>(tr_operand_dma(ot_, to0, to1, o), bp[t], dvacc[db]);
-                    dkacc[db] = mfma32<T>(tr_operand_dma(qt_, to0, to1, o), bds[t], dkacc[db]);
-                }
-            sched_reads_ahead<8, DB * 4, 2>();
-            prio_normal();
+        for (int i = 0; i < 2 * KS; ++i) {
+            if (i & 1) dp = mfma32<T>(fa[i], vf[i >> 1], dp);
+            else s = mfma32<T>(fa[i], kf[i >> 1], s);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // stats[sb ^ 1] held the previous tile's statistics, which every wave has finished
-        if (more) store_stats(sb ^ 1);
-        wait_dma();
-        __syncthreads();
     };
-    if constexpr (!BS) {
-        for (int it = tr.first; it < tr.full_first; ++it) step(it, it + 1, it - tr.first & 1, Flag<true>{});
-        for (int it = tr.full_first; it < tr.full_end; ++it) step(it, it + 1, it - tr.first & 1, Flag<false>{});
-        for (int it = tr.full_end; it < tr.end; ++it) step(it, it + 1, it - tr.first & 1, Flag<true>{});
-    } else {
-        for (int it = i0, sb = 0; it < tr.end; sb ^= 1) {
-            const int in = next_tile(it);
-            if (it < tr.full_first || it >= tr.full_end) step(it, in, sb, Flag<true>{});
-            else step(it, in, sb, Flag<false>{});
-            it = in;
+    // dV^T += dO^T P and dK^T += Q^T dS of a previous block (qb QP, buffer bq;
+    // skipped when PREV is false), interleaved with P = exp(scale s - lse),
+    // dS = P o (dP - D) of the current block (qb QC, first row qb0, statistics
+    // in buffer b), packed as B operands.  MFMA i: 32-row block i / 4 of d,
+    // k-half (i / 2) % 2, dV (i even, dO^T read transposed) or dK (i odd,
+    // Q^T); vector step e: element e of the current block.
+    auto part_bv = [&](auto prev_tag, int bq, auto qp_tag, const u32x4 (&bpp)[2], const u32x4 (&bdp)[2], int b, int qb0,
+                       auto qc_tag, auto masked_tag, const f32x16& s, const f32x16& dp, u32x4 (&bpo)[2],
+                       u32x4 (&bdo)[2]) __attribute__((always_inline)) {
+        constexpr bool PREV = decltype(prev_tag)::value;
+        constexpr int QP = decltype(qp_tag)::value;
+        constexpr int QC = decltype(qc_tag)::value;
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        constexpr int NB = 4 * DB;  // MFMAs of the previous block: one every 16 / NB elements
+        const char* qt_ = (const char*)(smem + 2 * bq * TB);
+        const char* ot_ = (const char*)(smem + (2 * bq + 1) * TB);
+        auto rd = [&](int i) __attribute__((always_inline)) {
+            return tr_operand_dma((i & 1) ? qt_ : ot_, to0, to1, DT::tr_blk(2 * QP + ((i >> 1) & 1), i >> 2));
+        };
+        // row statistics of the query rows this lane holds: 8g + 4h + (0..3)
+        f32x4 l4[4], d4[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            l4[g] = *(const f32x4*)(&stats[b][0][32 * QC + 8 * g + 4 * h]);
+            d4[g] = *(const f32x4*)(&stats[b][1][32 * QC + 8 * g + 4 * h]);
         }
+        u32x4 ta[NB];
+        if (PREV) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i) ta[i] = rd(i);
+        }
+        float pv[16], dv[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            if (PREV && (e * NB) % 16 == 0) {
+                const int i = e * NB / 16;
+                if (i & 1) dkacc[i >> 2] = mfma32<T>(ta[i], bdp[(i >> 1) & 1], dkacc[i >> 2]);
+                else dvacc[i >> 2] = mfma32<T>(ta[i], bpp[(i >> 1) & 1], dvacc[i >> 2]);
+            }
+            const int i = e;
+            const int g = i >> 2, r = i & 3;
+            float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -l4[g][r]));
+            if constexpr (MASKED) {
+                if (!sq.visible(qb0 + 8 * g + 4 * h + r, krow)) pe = 0.f;
+            }
+            pv[i] = pe;
+            dv[i] = pe * (dp[i] - d4[g][r]);
+            if (i & 1) {
+                bpo[i >> 3][(i & 7) >> 1] = pack2<T>(pv[i - 1], pv[i]);
+                bdo[i >> 3][(i & 7) >> 1] = pack2<T>(dv[i - 1], dv[i]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // Pin the packed results here: they are used only by the next
+        // block's products, and the compiler would otherwise sink this whole
+        // vector computation past the tile barrier, out of the MFMA shadow.
+        asm volatile("" : "+v"(bpo[0]), "+v"(bpo[1]), "+v"(bdo[0]), "+v"(bdo[1]));
+    };
+    // dV, dK products alone (the walk's last block).
+    auto part_b = [&](int bq, auto qp_tag, const u32x4 (&bpp)[2], const u32x4 (&bdp)[2]) __attribute__((always_inline)) {
+        constexpr int QP = decltype(qp_tag)::value;
+        const char* qt_ = (const char*)(smem + 2 * bq * TB);
+        const char* ot_ = (const char*)(smem + (2 * bq + 1) * TB);
+#pragma unroll
+        for (int i = 0; i < 4 * DB; ++i) {
+            const u32x4 a = tr_operand_dma((i & 1) ? qt_ : ot_, to0, to1, DT::tr_blk(2 * QP + ((i >> 1) & 1), i >> 2));
+            if (i & 1) dkacc[i >> 2] = mfma32<T>(a, bdp[(i >> 1) & 1], dkacc[i >> 2]);
+            else dvacc[i >> 2] = mfma32<T>(a, bpp[(i >> 1) & 1], dvacc[i >> 2]);
+        }
+    };
+
+    // Per-wave pipeline registers: S, dP of the current block; packed P, dS
+    // of the blocks with index 0 / 1 in their tile.
+    f32x16 sc, dpc;
+    u32x4 bp[2][2], bds[2][2];
+
+    // Walk state: tiles it (position n in the walk, ring buffer bc), in1 and
+    // in2 (the next two); bn and bpv are the buffers of positions n + 1 and
+    // n - 1 (== n + 2).
+    int it = tr.first;
+    if (BS)
+        while (it < tr.end && !bmcol[(size_t)(it >> 1) * sq.nb]) ++it;
+    int in1 = it < tr.end ? next_tile(it) : tr.end;
+    int in2 = in1 < tr.end ? next_tile(in1) : tr.end;
+    int bc = 0, bn = 1, bpv = 2;
+    if (it < tr.end) {
+        fetch(it, 0);
+        store_stats(0);
+        if (in1 < tr.end) fetch(in1, 1);  // its statistics are stored at the first tile boundary
+    }
+    wait_dma();  // unconditional (see the dq kernel)
+    __syncthreads();
+    if (it < tr.end) {
+        // One tile: for each of its two blocks, S and dP on the matrix cores,
+        // then P and dS on the vector unit while the matrix cores run the dV,
+        // dK products of the block before (FIRST: the walk's first tile has
+        // none before its block 0).
+        auto tile = [&](auto masked_tag, auto first_tag) __attribute__((always_inline)) {
+            constexpr bool FIRST = decltype(first_tag)::value;
+            const int qq0 = it * kK_BQ;
+            prio_mfma();
+            part_a(bc, Flag<0>{}, sc, dpc);
+            part_bv(Flag<!FIRST>{}, bpv, Flag<1>{}, bp[1], bds[1], bc, qq0, Flag<0>{}, masked_tag, sc, dpc, bp[0], bds[0]);
+            part_a(bc, Flag<1>{}, sc, dpc);
+            part_bv(Flag<true>{}, bc, Flag<0>{}, bp[0], bds[0], bc, qq0 + 32, Flag<1>{}, masked_tag, sc, dpc, bp[1], bds[1]);
+            prio_normal();
+        };
+        // Tile boundary: every wave has finished tile it and the previous
+        // one (apart from block 1 of tile it, whose dV, dK products run with
+        // the next tile), the DMA of tile in1 has landed, and tile in2 goes
+        // into the buffer of the previous tile.
+        auto boundary = [&]() __attribute__((always_inline)) {
+            wait_dma();
+            if (in1 < tr.end) store_stats(bn);
+            __syncthreads();
+            if (in2 < tr.end) fetch(in2, bpv);
+            it = in1;
+            in1 = in2;
+            in2 = in2 < tr.end ? next_tile(in2) : tr.end;
+            const int b0 = bpv;
+            bpv = bc;
+            bc = bn;
+            bn = b0;
+        };
+        auto masked_tile = [&](int t) { return t < tr.full_first || t >= tr.full_end; };
+
+        if (masked_tile(it)) tile(Flag<true>{}, Flag<true>{});
+        else tile(Flag<false>{}, Flag<true>{});
+        boundary();
+        // The visited tiles ascend, and the masked ones lie before full_first
+        // or from full_end on: one loop per kind, so that each loop body has
+        // a single register assignment (a loop whose body branches between
+        // the two kinds has the compiler copy the accumulators every tile).
+        auto run = [&](int lim, auto masked_tag) __attribute__((always_inline)) {
+            while (it < lim) {
+                tile(masked_tag, Flag<false>{});
+                boundary();
+            }
+        };
+        run(tr.full_first, Flag<true>{});
+        run(tr.full_end, Flag<false>{});
+        run(tr.end, Flag<true>{});
+        // block 1 of the last tile (now the previous buffer)
+        prio_mfma();
+        part_b(bpv, Flag<1>{}, bp[1], bds[1]);
+        prio_normal();
     }
 
+    // the ring buffers are reused as output staging
+    __syncthreads();
     stage_transposed<T, D, STR>(smem, 32 * w + n32, h, dkacc, scale);
     __syncthreads();
     store_staged<D, STR>(dK + sq.krow0 * D, smem, kK_BK, k0, nk, tid);
