@@ -4,7 +4,7 @@ A step is one pass of the whole hot path over one batch of synthetic input:
 the forward (O and lse) and the recompute backward (dQ, dK, dV) of
 B=1, H=32, N=8192, d=128, causal, bf16 attention with inputs resident in HBM.
 
-    python bench.py [--steps K] [--warmup W] [--passes fwd|fwdbwd] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--passes fwd|fwdbwd] [--no-cpu-baseline] [--no-extras]
                     [--workload headline|window512|varlen|blocksparse|io] [--n N]
 
 The default (headline) workload is the one above.  `window512` runs the same
@@ -22,6 +22,13 @@ JSON line.  Throughput is algorithmic FLOP/s: forward
 the score recomputation included), pairs = N(N+1)/2 per head when causal.
 Kernel durations come from HIP events recorded on the stream the library
 launches on (torch's current stream).
+
+The headline run also reports, outside the timed region, (i) the instruction
+rates of the part measured by the rate_probe executable (v_exp_f32, fp32 FMA
+and bf16 MFMA per CU per shader cycle) with the time those rates put under
+the passes' exponentials, and (ii) the shader clock sampled with rocm-smi
+while each pass runs back to back for about a second (the part lowers its
+clock under sustained load).
 """
 from __future__ import annotations
 
@@ -30,6 +37,8 @@ import json
 import math
 import os
 import platform
+import re
+import subprocess
 import sys
 import time
 
@@ -50,9 +59,9 @@ METRIC = "fused attention fwd/bwd TFLOP/s and % MFMA peak, N=8192 d=128 causal b
 # them; for any other code the traffic is reported as null.
 TRAFFIC_SOURCES = ("attn_device.h", "attn_launch.h", "attn_fwd.hip", "attn_bwd.hip")
 TRAFFIC = {
-    "sha256": "aa54eacec0f9f8d85995837cac70ade033e3899e1678f8cfa1fef3538f78ae7e",
-    "fwd": 289471898,             # attn_fwd_kernel: fetch 2 x 108063.7 KiB + write 66560.0 KiB
-    "bwd": 501436211 + 424085504,  # attn_bwd_dq_kernel (2 x 211561.9 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 141537.0 + 131072.0 KiB)
+    "sha256": "38c7389a2d60ef0bcfec5d28dde3d20888ddafabbea67a82af63ad5fbf370d62",
+    "fwd": 289693491,             # attn_fwd_kernel: fetch 2 x 108171.9 KiB + write 66560.0 KiB
+    "bwd": 500551680 + 422102016,  # attn_bwd_dq_kernel (2 x 211130.0 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 140568.5 + 131072.0 KiB)
 }
 
 
@@ -73,6 +82,45 @@ def kernel_code_digest():
 
 def measured_traffic(which):
     return TRAFFIC[which] if kernel_code_digest() == TRAFFIC["sha256"] else None
+
+
+def run_rate_probe():
+    """Instruction rates from the rate_probe executable (None if it is absent or fails)."""
+    exe = os.path.join(ROOT, "io_aware_exact_06_amd", "rate_probe")
+    if not os.path.exists(exe):
+        return None
+    try:
+        r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+        return json.loads(r.stdout.strip().splitlines()[-1]) if r.returncode == 0 else None
+    except (OSError, ValueError, IndexError, subprocess.TimeoutExpired):
+        return None
+
+
+def sample_sclk(run_for, seconds=1.2, samples=3):
+    """Shader clock (MHz) read with rocm-smi while run_for() keeps the GPU busy.
+
+    run_for(n) enqueues n passes; enough are queued for `seconds`, the clock
+    is sampled `samples` times while they run.  Returns the samples, or None.
+    """
+    import torch
+    try:
+        t0 = time.perf_counter()
+        run_for(10)
+        torch.cuda.synchronize()
+        per = (time.perf_counter() - t0) / 10
+        run_for(max(10, int(seconds / max(per, 1e-5))))
+        got = []
+        for _ in range(samples):
+            time.sleep(seconds / (samples + 1))
+            r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+            m = re.search(r"sclk clock level:\s*\d+:\s*\((\d+)Mhz\)", r.stdout)
+            if m:
+                got.append(int(m.group(1)))
+        torch.cuda.synchronize()
+        return got or None
+    except (OSError, subprocess.TimeoutExpired):
+        torch.cuda.synchronize()
+        return None
 
 
 def flops(w, passes):
@@ -319,6 +367,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--passes", choices=["fwd", "fwdbwd"], default="fwdbwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the instruction-rate probe and the clock sampling (profiling runs)")
     ap.add_argument("--workload", choices=["headline", "window512", "varlen", "blocksparse", "io"],
                     default="headline")
     ap.add_argument("--n", type=int, default=4096, help="sequence length of the io workload")
@@ -346,6 +396,7 @@ def main():
         bench_packed(args, args.workload)
         return
 
+    rates = None if args.no_extras else run_rate_probe()  # before this process touches the GPU
     w = WORKLOADS[WORKLOAD_INDEX]
     scale = default_scale(w.d)
     inp = workload_inputs(WORKLOAD_INDEX)
@@ -428,6 +479,20 @@ def main():
     if bwd:
         out["bwd"] = {"median_ms": round(med(bwd_ms), 4), "min_ms": round(bwd_ms[0], 4),
                       "tflops": round(b_tf, 2), "pct_peak": round(100 * b_tf / PEAK_BF16_TFLOPS, 2)}
+    # Secondary roof: the exponentials (one per unmasked pair in the forward,
+    # one per pair in each backward kernel) at the probe's v_exp_f32 rate, on
+    # all CUs at the nominal 2.4 GHz.
+    if rates:
+        exps_fwd = w.pairs_per_head() * w.B * w.H
+        exp_rate = rates["exp_per_clk_per_cu"] * rates["cus"] * 2.4e9
+        out["rates"] = dict(rates)
+        out["exp_bound_ms"] = {"fwd": round(exps_fwd / exp_rate * 1e3, 4),
+                               "bwd": round(2 * exps_fwd / exp_rate * 1e3, 4) if bwd else None}
+    fwd_only = lambda n: [attn.fwd(q, k, v, w.causal, scale, o=o, lse=lse) for _ in range(n)]
+    bwd_only = lambda n: [attn.bwd(q, k, v, o, do, lse, w.causal, scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+                          for _ in range(n)]
+    if not args.no_extras:
+        out["sclk_mhz_sustained"] = {"fwd": sample_sclk(fwd_only), "bwd": sample_sclk(bwd_only) if bwd else None}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, scale, args.passes)
     print(json.dumps(out), flush=True)

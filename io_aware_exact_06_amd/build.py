@@ -2,7 +2,9 @@
 
 Usage: python -m io_aware_exact_06_amd.build   (or __graft_entry__.build()).
 Every HIP source is compiled with packed-fp32 instructions disabled; the
-objects are linked into one shared library next to this file.
+objects are linked into one shared library next to this file.  The
+instruction-rate probe (csrc/rate_probe.hip) becomes the executable
+rate_probe beside it.
 """
 from __future__ import annotations
 
@@ -17,6 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libattn.so")
+PROBE = os.path.join(HERE, "rate_probe")  # instruction-rate microbenchmark (an executable)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -39,10 +42,21 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _build_probe() -> None:
+    tmp = PROBE + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *COMMON, "-x", "hip", os.path.join(CSRC, "rate_probe.hip"), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for rate_probe.hip:\n" + r.stdout + r.stderr)
+    os.replace(tmp, PROBE)
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with cf.ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        probe = ex.submit(_build_probe)
         objs = list(ex.map(_compile, SOURCES))
+        probe.result()
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

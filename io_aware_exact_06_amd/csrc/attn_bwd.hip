@@ -287,7 +287,7 @@ constexpr int kK_BQ = 64;
 constexpr int kK_NBUF = 3;
 
 template <class T, int D, bool BS>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(D == 64 ? 2 : 1, 2)))
 void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                           const float* __restrict__ LSE, const float* __restrict__ Delta,
