@@ -319,32 +319,46 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             }
         }
     } else {
-        // Walk the active tiles, each with the per-element test (exact for
-        // every tile); two steps per iteration, of fixed parities, as in the
-        // dense loop, and the last tile after the loop.
+        // Walk the active tiles: two steps per iteration, of fixed parities,
+        // as in the dense loop, and the last tile (which has no successor)
+        // after the loops.  Masked tiles (those some row of the group does
+        // not see whole) lie before full_first or from full_end on; the
+        // interior tiles of active blocks take the unmasked step.  One loop
+        // per kind: a loop whose body branched between the two kinds would
+        // have the compiler copy the accumulators every tile.
         int jt = j0, jn = j1;
-        if (jt < tr.end && jn < tr.end && (jt & 1)) {
-            const int jn2 = next_tile(jn);
-            step(jt, jn, jn2, Flag<1>{}, Flag<true>{}, Flag<true>{});
-            jt = jn;
-            jn = jn2;
-        }
-        while (jn < tr.end) {  // jt is even and has a successor
-            const int jn2 = next_tile(jn);
-            step(jt, jn, jn2, Flag<0>{}, Flag<true>{}, Flag<true>{});
-            if (jn2 >= tr.end) {
+        // Steps for the tiles jt < lim that have a successor.
+        auto run = [&](int lim, auto masked_tag) __attribute__((always_inline)) {
+            if (jt < lim && jn < tr.end && (jt & 1)) {
+                const int jn2 = next_tile(jn);
+                step(jt, jn, jn2, Flag<1>{}, masked_tag, Flag<true>{});
                 jt = jn;
                 jn = jn2;
-                break;
             }
-            const int jn3 = next_tile(jn2);
-            step(jn, jn2, jn3, Flag<1>{}, Flag<true>{}, Flag<true>{});
-            jt = jn2;
-            jn = jn3;
-        }
+            while (jt < lim && jn < tr.end) {  // jt is even
+                int jn2 = next_tile(jn);
+                step(jt, jn, jn2, Flag<0>{}, masked_tag, Flag<true>{});
+                jt = jn;
+                jn = jn2;
+                if (jt >= lim || jn >= tr.end) break;
+                jn2 = next_tile(jn);
+                step(jt, jn, jn2, Flag<1>{}, masked_tag, Flag<true>{});
+                jt = jn;
+                jn = jn2;
+            }
+        };
+        run(tr.full_first, Flag<true>{});
+        run(tr.full_end, Flag<false>{});
+        run(tr.end, Flag<true>{});
         if (jt < tr.end) {  // the last tile
-            if (jt & 1) step(jt, tr.end, tr.end, Flag<1>{}, Flag<true>{}, Flag<false>{});
-            else step(jt, tr.end, tr.end, Flag<0>{}, Flag<true>{}, Flag<false>{});
+            const bool last_masked = jt < tr.full_first || jt >= tr.full_end;
+            if (jt & 1) {
+                if (last_masked) step(jt, tr.end, tr.end, Flag<1>{}, Flag<true>{}, Flag<false>{});
+                else step(jt, tr.end, tr.end, Flag<1>{}, Flag<false>{}, Flag<false>{});
+            } else {
+                if (last_masked) step(jt, tr.end, tr.end, Flag<0>{}, Flag<true>{}, Flag<false>{});
+                else step(jt, tr.end, tr.end, Flag<0>{}, Flag<false>{}, Flag<false>{});
+            }
         }
     }
     __syncthreads();  // every wave is done with the tile buffers
