@@ -59,9 +59,9 @@ METRIC = "fused attention fwd/bwd TFLOP/s and % MFMA peak, N=8192 d=128 causal b
 # them; for any other code the traffic is reported as null.
 TRAFFIC_SOURCES = ("attn_device.h", "attn_launch.h", "attn_fwd.hip", "attn_bwd.hip")
 TRAFFIC = {
-    "sha256": "38c7389a2d60ef0bcfec5d28dde3d20888ddafabbea67a82af63ad5fbf370d62",
-    "fwd": 289693491,             # attn_fwd_kernel: fetch 2 x 108171.9 KiB + write 66560.0 KiB
-    "bwd": 500551680 + 422102016,  # attn_bwd_dq_kernel (2 x 211130.0 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 140568.5 + 131072.0 KiB)
+    "sha256": "dd8b2de95a9c5e982433835beee853ead1dc3fbc27b6e0c05221ab2c8edb921b",
+    "fwd": 288891290,             # attn_fwd_kernel: fetch 2 x 107780.2 KiB + write 66560.0 KiB
+    "bwd": 500824474 + 426738074,  # attn_bwd_dq_kernel (2 x 211263.2 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 142832.2 + 131072.0 KiB)
 }
 
 

@@ -256,12 +256,21 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
         for (int jt = tr.full_first; jt < tr.full_end; ++jt) step(jt, jt + 1, jt - tr.first & 1, Flag<false>{});
         for (int jt = tr.full_end; jt < tr.end; ++jt) step(jt, jt + 1, jt - tr.first & 1, Flag<true>{});
     } else {
-        for (int jt = j0, buf = 0; jt < tr.end; buf ^= 1) {
-            const int jn = next_tile(jt);
-            if (jt < tr.full_first || jt >= tr.full_end) step(jt, jn, buf, Flag<true>{});
-            else step(jt, jn, buf, Flag<false>{});
-            jt = jn;
-        }
+        // The visited tiles ascend; masked ones lie before full_first or from
+        // full_end on.  One loop per kind: a loop whose body branched between
+        // the kinds would have the compiler copy the accumulators every tile.
+        int jt = j0, buf = 0;
+        auto run = [&](int lim, auto masked_tag) __attribute__((always_inline)) {
+            while (jt < lim) {
+                const int jn = next_tile(jt);
+                step(jt, jn, buf, masked_tag);
+                jt = jn;
+                buf ^= 1;
+            }
+        };
+        run(tr.full_first, Flag<true>{});
+        run(tr.full_end, Flag<false>{});
+        run(tr.end, Flag<true>{});
     }
 
     stage_transposed<T, D, STR>(smem, 32 * w + n32, h, dqacc, scale);
