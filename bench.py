@@ -59,7 +59,7 @@ METRIC = "fused attention fwd/bwd TFLOP/s and % MFMA peak, N=8192 d=128 causal b
 # them; for any other code the traffic is reported as null.
 TRAFFIC_SOURCES = ("attn_device.h", "attn_launch.h", "attn_fwd.hip", "attn_bwd.hip")
 TRAFFIC = {
-    "sha256": "dd8b2de95a9c5e982433835beee853ead1dc3fbc27b6e0c05221ab2c8edb921b",
+    "sha256": "514ebaa7b71806328b05f68a7e0d6373a53e38b27f8542c7bef4dee6bb7d1e10",
     "fwd": 288891290,             # attn_fwd_kernel: fetch 2 x 107780.2 KiB + write 66560.0 KiB
     "bwd": 500824474 + 426738074,  # attn_bwd_dq_kernel (2 x 211263.2 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 142832.2 + 131072.0 KiB)
 }

@@ -455,17 +455,16 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
                 if (i & 1) dkacc[i >> 2] = mfma32<T>(ta[i], bdp[(i >> 1) & 1], dkacc[i >> 2]);
                 else dvacc[i >> 2] = mfma32<T>(ta[i], bpp[(i >> 1) & 1], dvacc[i >> 2]);
             }
-            const int i = e;
-            const int g = i >> 2, r = i & 3;
-            float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -l4[g][r]));
+            const int g = e >> 2, r = e & 3;
+            float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -l4[g][r]));
             if constexpr (MASKED) {
                 if (!sq.visible(qb0 + 8 * g + 4 * h + r, krow)) pe = 0.f;
             }
-            pv[i] = pe;
-            dv[i] = pe * (dp[i] - d4[g][r]);
-            if (i & 1) {
-                bpo[i >> 3][(i & 7) >> 1] = pack2<T>(pv[i - 1], pv[i]);
-                bdo[i >> 3][(i & 7) >> 1] = pack2<T>(dv[i - 1], dv[i]);
+            pv[e] = pe;
+            dv[e] = pe * (dp[e] - d4[g][r]);
+            if (e & 1) {
+                bpo[e >> 3][(e & 7) >> 1] = pack2<T>(pv[e - 1], pv[e]);
+                bdo[e >> 3][(e & 7) >> 1] = pack2<T>(dv[e - 1], dv[e]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
