@@ -129,3 +129,36 @@ def test_blocksparse_large_sampled_rows():
         rep = o_report(o[h, rows], ro[0], "bf16")
         assert rep["ok"], (h, rep)
         check_lse(lse[h, rows], rl[0], "head %d" % h)
+
+
+def sample(n, rng, extra=40):
+    fixed = [0, 1, 63, 64, 127, 128, 129, n // 2, n - 2, n - 1]
+    s = set(r for r in fixed if 0 <= r < n)
+    s.update(int(x) for x in rng.choice(n, size=min(extra, n), replace=False))
+    return np.array(sorted(s))
+
+
+def test_blocksparse_bwd_large_sampled():
+    """N = 4096, d = 128, bf16, causal, half of the blocks active (a mask per
+    head): sampled dQ rows and dK, dV keys against the oracle.  Long walks
+    with many skipped blocks, through both backward kernels."""
+    say("blocksparse bwd large sampled")
+    B, H, N, d = 1, 4, 4096, 128
+    nb = N // MB
+    mask = random_mask(H, nb, 0.5, seed=13)
+    inp = make_inputs(B, H, N, d, "bf16", seed=14, with_dout=True)
+    q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "dout"))
+    scale = default_scale(d)
+    o, lse = attn.fwd_blocksparse(q, k, v, mask, True, scale)
+    dq, dk, dv = attn.bwd_blocksparse(q, k, v, o, do, lse, mask, True, scale)
+    torch.cuda.synchronize()
+    dq, dk, dv = (a.float().cpu().numpy().reshape(H, N, d) for a in (dq, dk, dv))
+    rng = np.random.default_rng(15)
+    rows, keys = sample(N, rng), sample(N, rng)
+    for h in (0, H - 1):
+        rq, rk, rv = oracle.bwd(heads(inp["q"])[h:h + 1], heads(inp["k"])[h:h + 1], heads(inp["v"])[h:h + 1],
+                                heads(inp["dout"])[h:h + 1], True, scale, rows=rows, keys=keys,
+                                block_mask=mask[h], block=(MB, MB))
+        errs = [rel_l2(dq[h, rows], rq[0]), rel_l2(dk[h, keys], rk[0]), rel_l2(dv[h, keys], rv[0])]
+        say("  head %d rel-L2 dq %.3g dk %.3g dv %.3g" % (h, *errs))
+        assert max(errs) <= GRAD_TOL, (h, errs)

@@ -109,3 +109,33 @@ def test_window_of_whole_sequence_equals_no_window():
     o2, l2 = attn.fwd_varlen(q, k, v, cu, cu, N, True, 0.125, window=(N, -1))
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_window_large_sampled():
+    """The 512-key causal window at N = 8192 (the window workload's shape,
+    with 2 heads) through the packed entry points: sampled rows of O, lse and
+    dQ, sampled keys of dK and dV, against the oracle."""
+    say("window 512, N = 8192, sampled")
+    H, N, d, win = 2, 8192, 128, (511, -1)
+    inp = make_inputs(1, H, N, d, "bf16", seed=31, with_dout=True)
+    q, k, v, do = (inp[n][0].cuda() for n in ("q", "k", "v", "dout"))
+    cu = torch.tensor([0, N], dtype=torch.int32, device="cuda")
+    scale = default_scale(d)
+    o, lse = attn.fwd_varlen(q, k, v, cu, cu, N, True, scale, win)
+    dq, dk, dv = attn.bwd_varlen(q, k, v, o, do, lse, cu, cu, N, N, True, scale, win)
+    torch.cuda.synchronize()
+    o, dq, dk, dv = (a.float().cpu().numpy() for a in (o, dq, dk, dv))
+    lse = lse.cpu().numpy()
+    rng = np.random.default_rng(32)
+    pick = [0, 1, 63, 64, 510, 511, 512, 513, 1023, 1024, N // 2, N - 2, N - 1]
+    rows = np.array(sorted(set(pick) | set(int(x) for x in rng.choice(N, 40, replace=False))))
+    keys = np.array(sorted(set(pick) | set(int(x) for x in rng.choice(N, 40, replace=False))))
+    Q, K, V, dO = (inp[n][0].double().numpy() for n in ("q", "k", "v", "dout"))
+    ro, rl = oracle.fwd(Q[:, rows], K, V, True, scale, qpos=rows, window=win)
+    rep = o_report(o[:, rows], ro, "bf16")
+    assert rep["ok"], rep
+    check_lse(lse[:, rows], rl, "window")
+    rq, rk, rv = oracle.bwd(Q, K, V, dO, True, scale, rows=rows, keys=keys, window=win)
+    errs = [rel_l2(dq[:, rows], rq), rel_l2(dk[:, keys], rk), rel_l2(dv[:, keys], rv)]
+    say("  O max_abs %.3g, grads %.3g %.3g %.3g" % (rep["max_abs"], *errs))
+    assert max(errs) <= GRAD_TOL, errs
