@@ -5,7 +5,7 @@ the forward (O and lse) and the recompute backward (dQ, dK, dV) of
 B=1, H=32, N=8192, d=128, causal, bf16 attention with inputs resident in HBM.
 
     python bench.py [--steps K] [--warmup W] [--passes fwd|fwdbwd] [--no-cpu-baseline] [--no-extras]
-                    [--workload headline|window512|varlen|blocksparse|io] [--n N]
+                    [--workload headline|window512|varlen|blocksparse|io|decode] [--n N]
 
 The default (headline) workload is the one above.  `window512` runs the same
 shape with a causal sliding window of 512 keys (local attention, through the
@@ -253,6 +253,64 @@ def bench_packed(args, workload):
     print(json.dumps(out), flush=True)
 
 
+def bench_decode(args):
+    """Decode shape: 32 sequences of one query row each against 8192 cached keys
+    (32 heads, d = 128, bf16, causal with rows aligned to the end of the keys)
+    through attn_fwd_varlen.  The pass reads every K and V row once, so the
+    roof is HBM bandwidth; the line reports the compulsory bytes (Q, K, V, O,
+    lse) per second against 8 TB/s."""
+    import numpy as np
+    import torch
+
+    from io_aware_exact_06_amd import attn
+    from io_aware_exact_06_amd.inputs import default_scale, make_inputs
+    nseq, nk, H, d = 32, 8192, 32, 128
+    lq, lk = [1] * nseq, [nk] * nseq
+    dev = torch.device("cuda:0")
+    a = make_inputs(1, H, sum(lq), d, "bf16", 1006)
+    b = make_inputs(1, H, sum(lk), d, "bf16", 1007)
+    q = a["q"][0].to(dev)
+    k, v = b["k"][0].to(dev), b["v"][0].to(dev)
+    cu_q = torch.from_numpy(np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)).to(dev)
+    cu_k = torch.from_numpy(np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)).to(dev)
+    scale = default_scale(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((H, sum(lq)), dtype=torch.float32, device=dev)
+
+    def run():
+        attn.fwd_varlen(q, k, v, cu_q, cu_k, max(lq), True, scale, o=o, lse=lse)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record()
+        run()
+        e[1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [e[0].elapsed_time(e[1]) for e in evs]
+    avg = sum(ms) / len(ms)
+    nbytes = 2 * H * d * (sum(lq) * 2 + sum(lk) * 2) + 4 * H * sum(lq)  # Q, O, K, V (16-bit) + lse
+    gbs = nbytes / (avg * 1e-3) / 1e9
+    out = {
+        "metric": "decode attention forward HBM GB/s", "value": round(gbs, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: iid N(0,1) fp32 rounded to bf16, seeds 1006, 1007",
+        "config": {"workload": "fwd_decode32_nq1_nk8192_H32_d128_bf16_causal", "sequences": nseq, "nq": 1,
+                   "nk": nk, "H": H, "d": d, "causal": True, "passes": "fwd"},
+        "fwd": {"avg_ms": round(avg, 4), "min_ms": round(min(ms), 4)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(gbs / 8000.0, 4), "traffic": None, "kernel": "attn_fwd_kernel (packed)",
+                     "compulsory_bytes": nbytes},
+        "outputs_finite": bool(torch.isfinite(o).all() and torch.isfinite(lse).all()),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def bench_blocksparse(args):
     """Headline shape with a per-head 50% random block mask (seed 2025), causal."""
     import numpy as np
@@ -369,7 +427,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the instruction-rate probe and the clock sampling (profiling runs)")
-    ap.add_argument("--workload", choices=["headline", "window512", "varlen", "blocksparse", "io"],
+    ap.add_argument("--workload", choices=["headline", "window512", "varlen", "blocksparse", "io", "decode"],
                     default="headline")
     ap.add_argument("--n", type=int, default=4096, help="sequence length of the io workload")
     args = ap.parse_args()
@@ -391,6 +449,9 @@ def main():
         return
     if args.workload == "blocksparse":
         bench_blocksparse(args)
+        return
+    if args.workload == "decode":
+        bench_decode(args)
         return
     if args.workload != "headline":
         bench_packed(args, args.workload)

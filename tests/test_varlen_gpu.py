@@ -139,3 +139,28 @@ def test_window_large_sampled():
     errs = [rel_l2(dq[:, rows], rq), rel_l2(dk[:, keys], rk), rel_l2(dv[:, keys], rv)]
     say("  O max_abs %.3g, grads %.3g %.3g %.3g" % (rep["max_abs"], *errs))
     assert max(errs) <= GRAD_TOL, errs
+
+
+def test_decode_and_cached_prefill_shapes():
+    """Rectangular packed batches at cache sizes: single-row decode steps and
+    short prefill chunks against up to 8192 cached keys (rows aligned to the
+    end of the keys, causal), forward and backward against the oracle."""
+    lq, lk, H, d, dtype = [1, 1, 64, 200, 3], [8192, 3000, 8192, 5000, 129], 2, 128, "bf16"
+    say("decode / cached prefill lq=%s lk=%s" % (lq, lk))
+    q, k, v, do, cu_q, cu_k = packed_inputs(lq, lk, H, d, dtype, seed=41)
+    scale = default_scale(d)
+    dev = torch.device("cuda")
+    gq, gk, gv, gdo = (t.to(dev) for t in (q, k, v, do))
+    tcq, tck = torch.from_numpy(cu_q).to(dev), torch.from_numpy(cu_k).to(dev)
+    o, lse = attn.fwd_varlen(gq, gk, gv, tcq, tck, max(lq), True, scale)
+    dq, dk, dv = attn.bwd_varlen(gq, gk, gv, o, gdo, lse, tcq, tck, max(lq), max(lk), True, scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.fwd_varlen(q.double().numpy(), k.double().numpy(), v.double().numpy(), cu_q, cu_k, True, scale)
+    rep = o_report(o.float().cpu().numpy(), ro, dtype)
+    assert rep["ok"], rep
+    check_lse(lse.cpu().numpy(), rl, "decode")
+    rq, rk, rv = oracle.bwd_varlen(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                   do.double().numpy(), cu_q, cu_k, True, scale)
+    errs = [rel_l2(a.float().cpu().numpy(), r) for a, r in ((dq, rq), (dk, rk), (dv, rv))]
+    say("  O max_abs %.3g, grads %.3g %.3g %.3g" % (rep["max_abs"], *errs))
+    assert max(errs) <= GRAD_TOL, errs
