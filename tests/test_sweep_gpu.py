@@ -39,7 +39,7 @@ def check(o, lse, grads, ro, rl, rgrads, dtype, label):
 def dense_cases():
     rng = np.random.default_rng(7001)
     out = []
-    for _ in range(8):
+    for _ in range(16):
         out.append((int(rng.integers(1, 3)), int(rng.integers(1, 4)), int(rng.integers(1, 700)),
                     int(rng.choice([64, 128])), str(rng.choice(["f16", "bf16"])), bool(rng.integers(2)),
                     int(rng.integers(1 << 30))))
@@ -65,7 +65,7 @@ def test_sweep_dense(B, H, N, d, dtype, causal, seed):
 def varlen_cases():
     rng = np.random.default_rng(7002)
     out = []
-    for _ in range(8):
+    for _ in range(16):
         n = int(rng.integers(1, 5))
         lq = [int(x) for x in rng.integers(0, 400, size=n)]
         if rng.integers(2):
@@ -107,7 +107,7 @@ def test_sweep_varlen(lq, lk, H, d, dtype, causal, window, seed):
 def blocksparse_cases():
     rng = np.random.default_rng(7003)
     out = []
-    for _ in range(8):
+    for _ in range(16):
         B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
         out.append((B, H, int(rng.integers(1, 900)), int(rng.choice([64, 128])), str(rng.choice(["f16", "bf16"])),
                     bool(rng.integers(2)), str(rng.choice(["1", "H", "BH"])), float(rng.uniform(0.1, 0.9)),
