@@ -119,3 +119,23 @@ def test_bwd_deterministic():
     a = gpu_fwd_bwd(inp, True, 0.09)
     b = gpu_fwd_bwd(inp, True, 0.09)
     assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("d,dtype", [(64, "f16"), (128, "bf16")])
+def test_bwd_scale_extremes(d, dtype):
+    """scale = 0 (uniform weights: dQ = dK = 0 exactly, dV = column sums of dO
+    over the rows that see each key) and a large scale (logits of standard
+    deviation about sqrt(d), nearly one-hot rows) against the oracle."""
+    B, H, N = 1, 2, 300
+    inp = make_inputs(B, H, N, d, dtype, seed=77 + d, with_dout=True)
+    for scale, causal in ((0.0, False), (0.0, True), (1.0, True), (1.0, False)):
+        say("bwd scale=%g causal=%d d=%d %s" % (scale, causal, d, dtype))
+        dq, dk, dv = (a.reshape(B * H, N, d) for a in gpu_fwd_bwd(inp, causal, scale))
+        rq, rk, rv = oracle.bwd(heads(inp["q"]), heads(inp["k"]), heads(inp["v"]), heads(inp["dout"]), causal, scale)
+        assert rel_l2(dv, rv) <= GRAD_TOL
+        if scale == 0.0:
+            assert np.all(dq == 0) and np.all(dk == 0)
+        else:
+            errs = [rel_l2(dq, rq), rel_l2(dk, rk), rel_l2(dv, rv)]
+            say("  rel-L2 dq %.3g dk %.3g dv %.3g" % tuple(errs))
+            assert max(errs) <= GRAD_TOL, errs
