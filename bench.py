@@ -55,22 +55,26 @@ METRIC = "fused attention fwd/bwd TFLOP/s and % MFMA peak, N=8192 d=128 causal b
 # --steps 3 --warmup 1`, scaled by what the same counters read for a plain 1 GiB
 # device copy (FETCH_SIZE reads half the copied bytes: factor 2.0; WRITE_SIZE
 # reads them exactly: factor 1.0).  The figures hold only for the kernel
-# code they were taken on, whose digest (kernel_code_digest) is stored beside
-# them; for any other code the traffic is reported as null.
+# code and device compile flags they were taken on, whose digest
+# (kernel_code_digest) is stored beside them; for any other code the traffic
+# is reported as null.
 TRAFFIC_SOURCES = ("attn_device.h", "attn_launch.h", "attn_fwd.hip", "attn_bwd.hip")
 TRAFFIC = {
-    "sha256": "514ebaa7b71806328b05f68a7e0d6373a53e38b27f8542c7bef4dee6bb7d1e10",
-    "fwd": 288891290,             # attn_fwd_kernel: fetch 2 x 107780.2 KiB + write 66560.0 KiB
-    "bwd": 500824474 + 426738074,  # attn_bwd_dq_kernel (2 x 211263.2 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 142832.2 + 131072.0 KiB)
+    "sha256": "4998f211dcc6df9677618c1e985d51b5af659ed3df67387df5ecafca56a07c37",
+    "fwd": 289741760,             # attn_fwd_kernel: fetch 2 x 108195.5 KiB + write 66560.0 KiB
+    "bwd": 498931552 + 422582144,  # attn_bwd_dq_kernel (2 x 210338.9 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 140802.9 + 131072.0 KiB)
 }
 
 
 def kernel_code_digest():
-    """SHA-256 of the kernel sources with comments and whitespace removed: a
-    change to the code changes it, a change to a comment does not."""
+    """SHA-256 of the device compile flags and the kernel sources with comments
+    and whitespace removed: a change to the code or its flags changes it, a
+    change to a comment does not."""
     import hashlib
     import re
+    from io_aware_exact_06_amd import build as _build
     h = hashlib.sha256()
+    h.update(" ".join(f for f in _build.COMMON if not f.startswith("-I")).encode())
     for f in TRAFFIC_SOURCES:
         with open(os.path.join(ROOT, "io_aware_exact_06_amd", "csrc", f), encoding="utf-8") as fh:
             text = fh.read()
