@@ -5,7 +5,7 @@ the forward (O and lse) and the recompute backward (dQ, dK, dV) of
 B=1, H=32, N=8192, d=128, causal, bf16 attention with inputs resident in HBM.
 
     python bench.py [--steps K] [--warmup W] [--passes fwd|fwdbwd] [--no-cpu-baseline] [--no-extras]
-                    [--workload headline|window512|varlen|blocksparse|io|decode] [--n N]
+                    [--workload headline|window512|varlen|blocksparse|io|decode|configs] [--n N]
 
 The default (headline) workload is the one above.  `window512` runs the same
 shape with a causal sliding window of 512 keys (local attention, through the
@@ -16,8 +16,9 @@ mask of 128 x 128 blocks, half of them active (attn_fwd_blocksparse /
 attn_bwd_blocksparse).  `io` times the fused forward against the unfused three-pass
 forward (B=1, H=8, N=--n, d=128, bf16, causal) and runs one plain 1 GiB device
 copy; run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE it gives each kernel's
-memory traffic, the copy serving as the counters' calibration.  Prints one
-JSON line.  Throughput is algorithmic FLOP/s: forward
+memory traffic, the copy serving as the counters' calibration.  `configs`
+times the forward (and the backward where there is one) of each of the five
+problem configurations.  Prints one JSON line.  Throughput is algorithmic FLOP/s: forward
 4*d*pairs, backward 10*d*pairs (five d-deep products per unmasked pair,
 the score recomputation included), pairs = N(N+1)/2 per head when causal.
 Kernel durations come from HIP events recorded on the stream the library
@@ -422,6 +423,63 @@ def bench_io(args):
                       "unfused": res["unfused"], "calibration_copy_bytes": 1 << 30}), flush=True)
 
 
+def bench_configs(args):
+    """Every problem configuration of the workload list, forward (and backward
+    where the configuration has one), timed with HIP events on the launch
+    stream; one JSON line with a row per configuration.  The small ones are
+    launch- or latency-bound and are reported, not held to the matrix roof."""
+    import torch
+
+    from io_aware_exact_06_amd import attn
+    from io_aware_exact_06_amd.inputs import WORKLOADS, default_scale, workload_inputs
+
+    dev = torch.device("cuda:0")
+    rows = []
+    for idx, w in enumerate(WORKLOADS):
+        inp = workload_inputs(idx)
+        q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+        scale = default_scale(w.d)
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        ff = 4.0 * w.d * w.pairs_per_head() * w.B * w.H
+        reps = max(args.steps, 200 if ff < 5e10 else 0)
+        fwd = lambda: attn.fwd(q, k, v, w.causal, scale, o=o, lse=lse)
+        for _ in range(args.warmup):
+            fwd()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        for _ in range(reps):
+            fwd()
+        e[1].record()
+        torch.cuda.synchronize()
+        f_ms = e[0].elapsed_time(e[1]) / reps
+        row = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dtype": w.dtype,
+               "causal": w.causal, "fwd_ms": round(f_ms, 5), "fwd_tflops": round(ff / f_ms / 1e9, 2),
+               "fwd_pct_peak": round(100 * ff / f_ms / 1e9 / PEAK_BF16_TFLOPS, 2)}
+        if w.backward:
+            do = inp["dout"].to(dev)
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+            ws = torch.empty(max(1, attn.attn_bwd_workspace_bytes(w.B, w.H, w.N, w.d)), dtype=torch.uint8,
+                             device=dev)
+            fb = 10.0 * w.d * w.pairs_per_head() * w.B * w.H
+            bwd = lambda: attn.bwd(q, k, v, o, do, lse, w.causal, scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+            for _ in range(args.warmup):
+                bwd()
+            e[0].record()
+            for _ in range(args.steps):
+                bwd()
+            e[1].record()
+            torch.cuda.synchronize()
+            b_ms = e[0].elapsed_time(e[1]) / args.steps
+            row.update({"bwd_ms": round(b_ms, 5), "bwd_tflops": round(fb / b_ms / 1e9, 2),
+                        "bwd_pct_peak": round(100 * fb / b_ms / 1e9 / PEAK_BF16_TFLOPS, 2)})
+        rows.append(row)
+        del q, k, v, o, lse
+    print(json.dumps({"metric": "fused attention fwd/bwd TFLOP/s per configuration", "unit": "TFLOP/s",
+                      "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "peak": PEAK_BF16_TFLOPS,
+                      "data": "synthetic: the configurations' seeded inputs", "configs": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -431,7 +489,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the instruction-rate probe and the clock sampling (profiling runs)")
-    ap.add_argument("--workload", choices=["headline", "window512", "varlen", "blocksparse", "io", "decode"],
+    ap.add_argument("--workload", choices=["headline", "window512", "varlen", "blocksparse", "io", "decode",
+                                           "configs"],
                     default="headline")
     ap.add_argument("--n", type=int, default=4096, help="sequence length of the io workload")
     args = ap.parse_args()
@@ -456,6 +515,9 @@ def main():
         return
     if args.workload == "decode":
         bench_decode(args)
+        return
+    if args.workload == "configs":
+        bench_configs(args)
         return
     if args.workload != "headline":
         bench_packed(args, args.workload)
