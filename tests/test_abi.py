@@ -26,6 +26,19 @@ def test_library_exports_every_declared_function():
         assert hasattr(L, n), n
 
 
+def test_missing_library_raises_instead_of_falling_back(monkeypatch, tmp_path):
+    """Without the built library every entry point fails loudly: there is no
+    other path that could compute attention."""
+    monkeypatch.setattr(attn, "LIB_PATH", str(tmp_path / "libattn.so"))
+    monkeypatch.setattr(attn, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        attn.lib()
+    with pytest.raises(RuntimeError, match="missing"):
+        attn.attn_status_string(0)
+    with pytest.raises(RuntimeError, match="missing"):
+        attn.attn_fwd(0, 0, 0, 0, 0, 1, 1, 4, 64, 0, 0.125, attn.ATTN_F16, 0)
+
+
 def test_status_strings():
     for s in range(8):
         assert attn.attn_status_string(s) and attn.attn_status_string(s) != "unknown status"
