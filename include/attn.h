@@ -24,8 +24,10 @@
  * (natural logarithm of the scaled logits).
  *
  * Supported values.  d in {64, 128}; dtype ATTN_F16 or ATTN_BF16; causal in
- * {0, 1}; scale finite and >= 0 (callers normally pass 1/sqrt(d)).  B, H,
- * N >= 0; a call with B*H*N == 0 does nothing and returns ATTN_OK (the
+ * {0, 1}; scale any finite float, negative and zero included (callers
+ * normally pass 1/sqrt(d); the pages fix no sign for it).  The kernels form
+ * the scaled logits in fp32, so scale * <q, k> must stay within fp32 range.
+ * B, H, N >= 0; a call with B*H*N == 0 does nothing and returns ATTN_OK (the
  * pointers are then not examined).  Any N >= 1 works, including lengths that
  * are not a multiple of the kernels' tiles.
  *
@@ -159,7 +161,10 @@ int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void
  * article's hybrid local/global attention uses (section 三.1), applied
  * exactly; key tiles outside every row's window are skipped, tiles inside
  * every row's window run unmasked.  A row that sees no key gets O = 0 and
- * lse = -inf.  window_left, window_right >= -1 (-1: unbounded).
+ * lse = -inf.  window_left, window_right >= -1 (-1: unbounded); a window of
+ * total_q + total_k or more reaches every key and is taken as unbounded.
+ * total_q + total_k must not exceed 2^30 (ATTN_E_SHAPE otherwise), so that
+ * every position and window bound fits a 32-bit integer on the device.
  *
  * max_seqlen_q (and max_seqlen_k for the backward) bound the grid: rows of a
  * longer sequence past that length are not computed and their outputs are

@@ -137,7 +137,7 @@ def _dtype_code(t) -> int:
         return ATTN_BF16
     if t.dtype == torch.float16:
         return ATTN_F16
-    raise TypeError("q/k/v must be float16 or bfloat16, got %s" % t.dtype)
+    raise ValueError("q/k/v must be float16 or bfloat16, got %s" % t.dtype)
 
 
 def _stream_handle(device):
@@ -145,15 +145,48 @@ def _stream_handle(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _on_gpu(q):
+    import torch
+    if not isinstance(q, torch.Tensor) or q.device.type != "cuda":
+        raise ValueError("q must be a tensor on a GPU device")
+
+
+def _need(t, name, shape, dtype, device):
+    """Raise ValueError unless t is a contiguous `dtype` tensor of `shape` on `device`."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s must be a torch tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _workspace(ws, need, device):
+    """Workspace bytes of a caller-supplied contiguous device tensor (any dtype), or a new one."""
+    import torch
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    if not isinstance(ws, torch.Tensor) or ws.device != device or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on %s" % device)
+    nbytes = ws.numel() * ws.element_size()
+    if nbytes < need:
+        raise ValueError("workspace holds %d bytes, %d needed" % (nbytes, need))
+    return ws, nbytes
+
+
 def _shape(q, *others):
+    _on_gpu(q)
     if q.dim() != 4:
         raise ValueError("expected [B, H, N, d] tensors")
-    for t in others:
-        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
-            raise ValueError("all tensors must share shape, dtype and device")
-    for t in (q, *others):
-        if not t.is_contiguous():
-            raise ValueError("tensors must be contiguous")
+    for i, t in enumerate(others):
+        _need(t, "input %d" % (i + 1), q.shape, q.dtype, q.device)
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
     return tuple(int(x) for x in q.shape)
 
 
@@ -167,6 +200,8 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, o=None, lse=N
         o = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _need(o, "o", q.shape, q.dtype, q.device)
+    _need(lse, "lse", (B, H, N), torch.float32, q.device)
     _check(attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                     B, H, N, d, causal, scale, _dtype_code(q), _stream_handle(q.device)))
     return o, lse
@@ -182,32 +217,35 @@ def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
-    need = attn_bwd_workspace_bytes(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _need(lse, "lse", (B, H, N), torch.float32, q.device)
+    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _need(t, name, q.shape, q.dtype, q.device)
+    workspace, ws_bytes = _workspace(workspace, attn_bwd_workspace_bytes(B, H, N, d), q.device)
     _check(attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                     lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
-                    causal, scale, _dtype_code(q), workspace.data_ptr(), workspace.numel(),
+                    causal, scale, _dtype_code(q), workspace.data_ptr(), ws_bytes,
                     _stream_handle(q.device)))
     return dq, dk, dv
 
 
 def _packed(q, k, v):
-    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
+    _on_gpu(q)
+    if q.dim() != 3 or not hasattr(k, "dim") or k.dim() != 3:
         raise ValueError("packed tensors are [H, total, d]")
     H, tq, d = (int(x) for x in q.shape)
-    if k.shape[0] != H or k.shape[2] != d or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k, v must share heads, d and dtype")
-    for t in (q, k, v):
-        if not t.is_contiguous():
-            raise ValueError("tensors must be contiguous")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    _need(k, "k", (H, int(k.shape[1]), d), q.dtype, q.device)
+    _need(v, "v", k.shape, q.dtype, q.device)
     return H, tq, int(k.shape[1]), d
 
 
-def _cu(cu, device):
+def _cu(cu, device, name="cu_seqlens"):
+    """Number of sequences described by a cumulative-offset tensor (batch + 1 int32 values)."""
     import torch
-    if not (cu.dtype == torch.int32 and cu.device == device and cu.is_contiguous()):
-        raise ValueError("cu_seqlens must be contiguous int32 tensors on the tensors' device")
+    if not (isinstance(cu, torch.Tensor) and cu.dtype == torch.int32 and cu.device == device
+            and cu.dim() == 1 and cu.numel() >= 1 and cu.is_contiguous()):
+        raise ValueError("%s must be a contiguous 1-D int32 tensor of batch + 1 offsets on %s" % (name, device))
     return int(cu.numel()) - 1
 
 
@@ -216,13 +254,15 @@ def fwd_varlen(q, k, v, cu_q, cu_k, max_seqlen_q: int, causal: bool = False, sca
     """Packed variable-length forward: q [H, total_q, d], k, v [H, total_k, d]."""
     import torch
     H, tq, tk, d = _packed(q, k, v)
-    batch = _cu(cu_q, q.device)
-    if _cu(cu_k, q.device) != batch:
+    batch = _cu(cu_q, q.device, "cu_seqlens_q")
+    if _cu(cu_k, q.device, "cu_seqlens_k") != batch:
         raise ValueError("cu_seqlens_q and cu_seqlens_k describe different batch sizes")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = torch.empty_like(q) if o is None else o
     lse = torch.empty((H, tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(o, "o", q.shape, q.dtype, q.device)
+    _need(lse, "lse", (H, tq), torch.float32, q.device)
     _check(attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                            cu_q.data_ptr(), cu_k.data_ptr(), batch, H, tq, tk, int(max_seqlen_q), d, causal,
                            int(window[0]), int(window[1]), scale, _dtype_code(q), _stream_handle(q.device)))
@@ -234,20 +274,25 @@ def bwd_varlen(q, k, v, o, dout, lse, cu_q, cu_k, max_seqlen_q: int, max_seqlen_
     """Backward of fwd_varlen: returns dq [H, total_q, d], dk, dv [H, total_k, d]."""
     import torch
     H, tq, tk, d = _packed(q, k, v)
-    batch = _cu(cu_q, q.device)
+    batch = _cu(cu_q, q.device, "cu_seqlens_q")
+    if _cu(cu_k, q.device, "cu_seqlens_k") != batch:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k describe different batch sizes")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    need = attn_bwd_varlen_workspace_bytes(H, tq)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    for t, name in ((o, "o"), (dout, "dout"), (dq, "dq")):
+        _need(t, name, q.shape, q.dtype, q.device)
+    for t, name in ((dk, "dk"), (dv, "dv")):
+        _need(t, name, k.shape, q.dtype, q.device)
+    _need(lse, "lse", (H, tq), torch.float32, q.device)
+    workspace, ws_bytes = _workspace(workspace, attn_bwd_varlen_workspace_bytes(H, tq), q.device)
     _check(attn_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cu_q.data_ptr(),
                            cu_k.data_ptr(), batch, H, tq, tk, int(max_seqlen_q), int(max_seqlen_k), d, causal,
                            int(window[0]), int(window[1]), scale, _dtype_code(q), workspace.data_ptr(),
-                           workspace.numel(), _stream_handle(q.device)))
+                           ws_bytes, _stream_handle(q.device)))
     return dq, dk, dv
 
 
@@ -269,11 +314,14 @@ def fwd_unfused(q, k, v, causal: bool = False, scale: float | None = None, o=Non
         scale = 1.0 / math.sqrt(d)
     o = torch.empty_like(q) if o is None else o
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need(o, "o", q.shape, q.dtype, q.device)
+    _need(lse, "lse", (B, H, N), torch.float32, q.device)
     need = attn_fwd_unfused_workspace_bytes(B, H, N)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if need == ctypes.c_size_t(-1).value:
+        raise ValueError("the unfused baseline takes B*H <= 65535 and N <= 2^24")
+    workspace, ws_bytes = _workspace(workspace, need, q.device)
     _check(attn_fwd_unfused(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d,
-                            causal, scale, _dtype_code(q), workspace.data_ptr(), workspace.numel(),
+                            causal, scale, _dtype_code(q), workspace.data_ptr(), ws_bytes,
                             _stream_handle(q.device)))
     return o, lse
 
@@ -302,6 +350,8 @@ def fwd_blocksparse(q, k, v, block_mask, causal: bool = False, scale: float | No
         o = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _need(o, "o", q.shape, q.dtype, q.device)
+    _need(lse, "lse", (B, H, N), torch.float32, q.device)
     _check(attn_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                 B, H, N, d, m.data_ptr(), mh, causal, scale, _dtype_code(q),
                                 _stream_handle(q.device)))
@@ -319,11 +369,12 @@ def bwd_blocksparse(q, k, v, o, dout, lse, block_mask, causal: bool = False, sca
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
-    need = attn_bwd_workspace_bytes(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _need(lse, "lse", (B, H, N), torch.float32, q.device)
+    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _need(t, name, q.shape, q.dtype, q.device)
+    workspace, ws_bytes = _workspace(workspace, attn_bwd_workspace_bytes(B, H, N, d), q.device)
     _check(attn_bwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
                                 lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
                                 m.data_ptr(), mh, causal, scale, _dtype_code(q), workspace.data_ptr(),
-                                workspace.numel(), _stream_handle(q.device)))
+                                ws_bytes, _stream_handle(q.device)))
     return dq, dk, dv

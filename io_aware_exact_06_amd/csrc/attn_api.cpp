@@ -33,7 +33,7 @@ int check_common(int B, int H, int N, int d, int causal, float scale, int dtype,
     if (d != 64 && d != 128) return ATTN_E_UNSUPPORTED;
     if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_E_UNSUPPORTED;
     if (causal != 0 && causal != 1) return ATTN_E_UNSUPPORTED;
-    if (!isfinite(scale) || scale < 0.f) return ATTN_E_UNSUPPORTED;
+    if (!isfinite(scale)) return ATTN_E_UNSUPPORTED;
     const int64_t bh = (int64_t)B * H;  // < 2^62
     // Every byte count below (B*H*N*d*4 at most, d <= 128) must fit in int64.
     if (bh != 0 && (int64_t)N > INT64_MAX / 512 / bh) return ATTN_E_SHAPE;
@@ -191,16 +191,27 @@ int check_varlen(const int* cu_q, const int* cu_k, int batch, int H, int total_q
     if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_E_UNSUPPORTED;
     if (causal != 0 && causal != 1) return ATTN_E_UNSUPPORTED;
     if (wl < -1 || wr < -1) return ATTN_E_UNSUPPORTED;
-    if (!isfinite(scale) || scale < 0.f) return ATTN_E_UNSUPPORTED;
+    if (!isfinite(scale)) return ATTN_E_UNSUPPORTED;
     if (batch == INT32_MAX) return ATTN_E_SHAPE;  // batch + 1 offsets must be addressable
+    if ((int64_t)total_q + total_k > ((int64_t)1 << 30)) return ATTN_E_SHAPE;
     if (batch > 0 && (!cu_q || !cu_k)) return ATTN_E_NULL;
     if (!aligned(cu_q, 4) || !aligned(cu_k, 4)) return ATTN_E_ALIGN;
     return ATTN_OK;
 }
 
+// A window reaching total_q + total_k positions or more covers every key of
+// every row (|pos - j| < total_q + total_k), so it is the unbounded window -1.
+// check_varlen bounds total_q + total_k by 2^30, which keeps the device's
+// position and window arithmetic (pos +- window) inside int32.
+int clamp_window(int w, int total_q, int total_k) {
+    return (int64_t)w >= (int64_t)total_q + total_k ? -1 : w;
+}
+
 attn::SeqLayout varlen_layout(const int* cu_q, const int* cu_k, int batch, int H, int total_q, int total_k,
                               int causal, int wl, int wr) {
-    return attn::SeqLayout{1, batch, H, 0, cu_q, cu_k, total_q, total_k, wl, causal ? 0 : wr, nullptr, 0, 0};
+    wl = clamp_window(wl, total_q, total_k);
+    wr = causal ? 0 : clamp_window(wr, total_q, total_k);
+    return attn::SeqLayout{1, batch, H, 0, cu_q, cu_k, total_q, total_k, wl, wr, nullptr, 0, 0};
 }
 
 }  // namespace

@@ -77,7 +77,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(QB == 1 ? 2 : 1, QB == 1 ? 2 : 1)))
 void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                     float* __restrict__ LSE, SeqLayout L, int ntq, float scale, float c) {
+                     float* __restrict__ LSE, SeqLayout L, int ntq, float scale, float c, uint32_t qflip) {
     using DT = DmaTile<D, kBK>;
     constexpr int KS = D / 16;                 // MFMA k-steps of S^T over d
     constexpr int DB = D / 32;                 // 32-row blocks of O^T
@@ -105,13 +105,15 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     const uint16_t* Vh = V + sq.krow0 * D;
     const int wq0 = q0 + w * 32 * QB;  // block qb of this wave starts at row wq0 + 32 qb
 
-    // Q^T fragments (B operand of S^T = K Q^T), resident for the whole loop.
+    // Q^T fragments (B operand of S^T = K Q^T), resident for the whole loop;
+    // qflip negates them (sign bits of both 16-bit halves) for a negative scale.
     u32x4 qf[QB][KS];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int qrow = min(wq0 + 32 * qb + n32, nq - 1);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qf[qb][ks] = *(const u32x4*)(Qh + (int64_t)qrow * D + 16 * ks + 8 * h);
+        for (int ks = 0; ks < KS; ++ks)
+            qf[qb][ks] = *(const u32x4*)(Qh + (int64_t)qrow * D + 16 * ks + 8 * h) ^ qflip;
     }
 
     const int qlast = min(q0 + BQ, nq) - 1;
@@ -393,6 +395,12 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 template <class T, int D, bool BS>
 hipError_t launch(const FwdParams& p) {
     constexpr int QB = BS ? 1 : ATTN_FWD_QB, BQ = kWaves * 32 * QB;
+    // A negative scale runs as |scale| with Q negated (a sign flip, exact in
+    // 16-bit storage): scale * <q, k> = |scale| * <-q, k> bit for bit, so the
+    // running maximum is always taken of the logits that the exponentials use.
+    const bool neg = p.scale < 0.f;
+    const float ascale = neg ? -p.scale : p.scale;
+    const uint32_t qflip = neg ? 0x80008000u : 0u;
     const int ntq = (p.max_nq + BQ - 1) / BQ;
     const int64_t nseq = (int64_t)p.L.B * p.L.H;
     const int64_t blocks = nseq * ntq;
@@ -400,8 +408,8 @@ hipError_t launch(const FwdParams& p) {
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((attn_fwd_kernel<T, D, QB, BS>), dim3((unsigned)blocks), dim3(kThreads), 0,
                        (hipStream_t)p.stream, (const uint16_t*)p.q, (const uint16_t*)p.k,
-                       (const uint16_t*)p.v, (uint16_t*)p.o, p.lse, p.L, ntq, p.scale,
-                       p.scale * kLog2e);
+                       (const uint16_t*)p.v, (uint16_t*)p.o, p.lse, p.L, ntq, ascale,
+                       ascale * kLog2e, qflip);
     return hipGetLastError();
 }
 

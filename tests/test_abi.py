@@ -71,13 +71,22 @@ def bwd(ws_bytes=None, ws=A + 0x900000, **kw):
     (dict(q=0), 1), (dict(o=0), 1), (dict(lse=0), 1),
     (dict(N=-1), 2), (dict(B=-3), 2),
     (dict(d=96), 3), (dict(d=32), 3), (dict(dtype=2), 3), (dict(causal=2), 3),
-    (dict(scale=float("nan")), 3), (dict(scale=float("inf")), 3), (dict(scale=-1.0), 3),
+    (dict(scale=float("nan")), 3), (dict(scale=float("inf")), 3), (dict(scale=-float("inf")), 3),
     (dict(q=A + 8), 4), (dict(o=A + 0x300002), 4), (dict(lse=A + 0x400002), 4),
     (dict(o=A + 0x100), 5), (dict(lse=A + 0x300000 + SZ - 4), 5), (dict(o=A + 0x200000), 5),
     (dict(B=1 << 30, H=1 << 30, N=1 << 20), 2),
 ])
 def test_fwd_rejects(kw, status):
     assert fwd(**kw) == status
+
+
+def test_any_finite_scale_is_accepted():
+    """Negative and zero scales pass validation (an empty problem returns
+    right after the checks, so nothing is launched)."""
+    for s in (-1.0, -0.125, -0.0, 0.0, 1e30, -1e30):
+        assert fwd(q=0, k=0, v=0, o=0, lse=0, N=0, scale=s) == 0
+        assert bwd(q=0, k=0, v=0, o=0, dout=0, lse=0, dq=0, dk=0, dv=0, ws=0, ws_bytes=0, N=0, scale=s) == 0
+        assert fwd_varlen(q=0, k=0, v=0, o=0, lse=0, tq=0, scale=s) == 0
 
 
 def test_fwd_empty_problem_is_a_no_op():
@@ -119,7 +128,8 @@ def fwd_varlen(q=A, k=A + 0x100000, v=A + 0x200000, o=A + 0x300000, lse=A + 0x40
 @pytest.mark.parametrize("kw,status", [
     (dict(cu_q=0), 1), (dict(q=0), 1), (dict(k=0), 1), (dict(lse=0), 1),
     (dict(batch=-1), 2), (dict(tq=-5), 2), (dict(max_q=-1), 2),
-    (dict(d=48), 3), (dict(wl=-2), 3), (dict(wr=-3), 3), (dict(causal=3), 3), (dict(scale=-0.5), 3),
+    (dict(d=48), 3), (dict(wl=-2), 3), (dict(wr=-3), 3), (dict(causal=3), 3), (dict(scale=float("nan")), 3),
+    (dict(tq=1 << 29, tk=(1 << 29) + 1), 2),
     (dict(cu_k=A + 0x500102), 4), (dict(o=A + 0x300008), 4),
     (dict(o=A + 0x100010), 5), (dict(lse=A + 0x500000 - 8), 5), (dict(o=A + 0x500000 - 16), 5),
 ])

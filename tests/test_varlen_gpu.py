@@ -111,6 +111,26 @@ def test_window_of_whole_sequence_equals_no_window():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def test_window_of_int32_max_is_unbounded():
+    """A window of 2^31 - 1 on either side reaches every key: the result equals
+    the unwindowed call bit for bit (no overflow of position + window)."""
+    say("int32-max window")
+    H, N, d = 2, 300, 128
+    inp = make_inputs(1, H, N, d, "bf16", seed=6, with_dout=True)
+    q, k, v, do = (inp[n][0].cuda() for n in ("q", "k", "v", "dout"))
+    cu = torch.tensor([0, 100, N], dtype=torch.int32, device="cuda")
+    big = 2 ** 31 - 1
+    for causal in (False, True):
+        o1, l1 = attn.fwd_varlen(q, k, v, cu, cu, 200, causal, 0.1)
+        o2, l2 = attn.fwd_varlen(q, k, v, cu, cu, 200, causal, 0.1, window=(big, big))
+        g1 = attn.bwd_varlen(q, k, v, o1, do, l1, cu, cu, 200, 200, causal, 0.1)
+        g2 = attn.bwd_varlen(q, k, v, o2, do, l2, cu, cu, 200, 200, causal, 0.1, window=(big, big))
+        torch.cuda.synchronize()
+        assert torch.isfinite(l1).all()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        assert all(torch.equal(a, b) for a, b in zip(g1, g2))
+
+
 def test_window_large_sampled():
     """The 512-key causal window at N = 8192 (the window workload's shape,
     with 2 heads) through the packed entry points: sampled rows of O, lse and
