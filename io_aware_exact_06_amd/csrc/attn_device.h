@@ -269,6 +269,22 @@ __device__ inline u32x4 tr_operand(const uint16_t* tile_at_lane, int row0, int c
     return a;
 }
 
+// a.lo + a.hi + acc for a dword holding two 16-bit values (v_dot2c against
+// (1, 1); the products are exact, the sum is taken in fp32).
+template <class T>
+__device__ inline float add_pair(uint32_t a, float acc);
+
+template <>
+__device__ inline float add_pair<BF16>(uint32_t a, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, 0x3f803f80u),
+                                           acc, false);
+}
+
+template <>
+__device__ inline float add_pair<F16>(uint32_t a, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
+}
+
 // Pack the 16 fp32 accumulator values of a 32x32 MFMA result (lane l: column
 // l % 32, rows 8*(e/4) + 4*(l/32) + e%4) into the B operands of two 16-deep
 // k-steps that contract over those rows: k-step t takes elements 8t .. 8t+7.

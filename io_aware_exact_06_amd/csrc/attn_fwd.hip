@@ -26,6 +26,14 @@
 // running sum, packing); then the P.V products of tile j run.  Independent
 // MFMA and VALU work of one wave overlap on the SIMD.
 //
+// Two running sums per row: l adds the fp32 exponentials and gives
+// lse = scale * m + ln l; lh adds the same exponentials after their rounding
+// to the 16-bit input type, i.e. exactly the weights the P.V product uses, and
+// normalises O = (sum_j P_j V_j) / lh.  The weights of O then sum to one
+// whatever the rounding of P: a row dominated by one key returns that key's
+// value row instead of it scaled by the rounding error of its weight (up to
+// 2^-9 relative in bf16, which for |V| > 5 alone exceeds a 1e-2 budget).
+//
 // Rescaling: the maximum m used for the exponentials is raised only when a
 // row's new maximum exceeds it by more than 2^8 in the exponent (exp2 units);
 // otherwise exponentials up to 2^8 are accumulated against the old m.  The
@@ -133,11 +141,14 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int e = 0; e < 16; ++e) oacc[qb][db][e] = 0.f;
-    float m[QB], l[QB];  // running maximum (raw score); this lane's share of the running sum
+    // running maximum (raw score); this lane's shares of the running sums of
+    // the exponentials (l) and of their 16-bit roundings (lh)
+    float m[QB], l[QB], lh[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         m[qb] = kNegInf;
         l[qb] = 0.f;
+        lh[qb] = 0.f;
     }
     f32x16 sacc[2][QB][2];  // scores of the tiles with even / odd index: [parity][query block][key block]
 
@@ -241,6 +252,7 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                 const float mnew = fmaxf(m[qb], mx);
                 const float alpha = (m[qb] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((m[qb] - mnew) * c);
                 l[qb] *= alpha;
+                lh[qb] *= alpha;
 #pragma unroll
                 for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -275,6 +287,14 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                 for (int i = 0; i < 4; ++i) l4[i] = (p[i] + p[i + 4]) + (p[i + 8] + p[i + 12]);
                 l[qb] += (l4[0] + l4[1]) + (l4[2] + l4[3]);
                 pack_acc_as_b<T>(p, pf[qb][kb][0], pf[qb][kb][1]);
+                // the rounded weights, two per dword, in two chains
+                float h0 = lh[qb], h1 = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    h0 = add_pair<T>(pf[qb][kb][0][i], h0);
+                    h1 = add_pair<T>(pf[qb][kb][1][i], h1);
+                }
+                lh[qb] = h0 + h1;
             }
         // O^T += V^T P^T: each V^T fragment read from LDS feeds QB MFMAs
         const char* vt = (const char*)(Vb + PAR * TB);
@@ -371,8 +391,9 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     for (int qb = 0; qb < QB; ++qb) {
         const int qrow = wq0 + 32 * qb + n32;
         const float lt = sum_with_other_half(l[qb]);
+        const float lht = sum_with_other_half(lh[qb]);
         // a row that sees no key at all: O = 0, lse = -inf
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        const float inv = lht > 0.f ? 1.f / lht : 0.f;
         if (h == 0 && qrow < nq) LSE[sq.qrow0 + qrow] = lt > 0.f ? m[qb] * scale + logf(lt) : kNegInf;
         const int orow = (w * 32 * QB + 32 * qb + n32) * STR;
 #pragma unroll
