@@ -65,7 +65,8 @@ enum attn_status {
     ATTN_E_ALIGN = 4,       /* a pointer is not aligned as required */
     ATTN_E_ALIAS = 5,       /* an output overlaps an input or another output */
     ATTN_E_WORKSPACE = 6,   /* backward workspace missing or smaller than required */
-    ATTN_E_HIP = 7          /* the HIP runtime reported an error at launch */
+    ATTN_E_HIP = 7,         /* the HIP runtime reported an error at launch */
+    ATTN_E_TOO_LARGE = 8    /* attn_bwd_noalloc: B*H*N exceeds ATTN_NOALLOC_MAX_ROWS */
 };
 
 /*
@@ -104,6 +105,29 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              const float* lse, void* dq, void* dk, void* dv,
              int B, int H, int N, int d, int causal, float scale, int dtype,
              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, harnesses
+ * that forbid allocation).  The D terms live in a fixed 4 MiB device array of
+ * the library instead of the caller's workspace: each GPU the library runs on
+ * holds one copy of it until the process ends.  The call itself allocates
+ * nothing.  Arguments, layout, results and errors are those of attn_bwd
+ * (results are bitwise equal to attn_bwd's), except:
+ *   - B*H*N must not exceed ATTN_NOALLOC_MAX_ROWS (1048576 query rows);
+ *     larger problems return ATTN_E_TOO_LARGE and enqueue nothing;
+ *   - every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents (nothing in it needs to start at zero).  Calls that
+ *     overlap on one GPU -- on different streams, or from different threads
+ *     without ordering -- race on it and give wrong gradients; callers must
+ *     serialise them (one stream, or events between streams);
+ *   - the first call on a device looks up the array's device address
+ *     (hipGetSymbolAddress); a failure there returns ATTN_E_HIP.
+ */
+#define ATTN_NOALLOC_MAX_ROWS 1048576
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv,
+                     int B, int H, int N, int d, int causal, float scale, int dtype, void* stream);
 
 /*
  * Block-sparse attention: the tile skipping of all-zero mask blocks that the

@@ -20,12 +20,13 @@ LIB_PATH = os.path.join(HERE, "libattn.so")
 ATTN_F16, ATTN_BF16 = 0, 1
 STATUS = {
     0: "ATTN_OK", 1: "ATTN_E_NULL", 2: "ATTN_E_SHAPE", 3: "ATTN_E_UNSUPPORTED",
-    4: "ATTN_E_ALIGN", 5: "ATTN_E_ALIAS", 6: "ATTN_E_WORKSPACE", 7: "ATTN_E_HIP",
+    4: "ATTN_E_ALIGN", 5: "ATTN_E_ALIAS", 6: "ATTN_E_WORKSPACE", 7: "ATTN_E_HIP", 8: "ATTN_E_TOO_LARGE",
 }
+NOALLOC_MAX_ROWS = 1048576  # ATTN_NOALLOC_MAX_ROWS
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_string",
            "attn_fwd_varlen", "attn_bwd_varlen", "attn_bwd_varlen_workspace_bytes",
            "attn_fwd_unfused", "attn_fwd_unfused_workspace_bytes",
-           "attn_fwd_blocksparse", "attn_bwd_blocksparse")
+           "attn_fwd_blocksparse", "attn_bwd_blocksparse", "attn_bwd_noalloc")
 MASK_BLOCK = 128  # ATTN_MASK_BLOCK
 
 _lib = None
@@ -52,6 +53,8 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd_workspace_bytes.restype = sz
         L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
         L.attn_bwd.restype = i
+        L.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+        L.attn_bwd_noalloc.restype = i
         L.attn_status_string.argtypes = [i]
         L.attn_status_string.restype = ctypes.c_char_p
         L.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, vp]
@@ -92,6 +95,11 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal, scale, dtype
              workspace, workspace_bytes, stream) -> int:
     return lib().attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, int(causal),
                           float(scale), dtype, workspace, workspace_bytes, stream)
+
+
+def attn_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal, scale, dtype, stream) -> int:
+    return lib().attn_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, int(causal), float(scale),
+                                  dtype, stream)
 
 
 def attn_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, batch, H, total_q, total_k, max_q, d, causal,
@@ -225,6 +233,22 @@ def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
                     lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
                     causal, scale, _dtype_code(q), workspace.data_ptr(), ws_bytes,
                     _stream_handle(q.device)))
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, causal: bool = False, scale: float | None = None):
+    """bwd into caller-owned dq, dk, dv with no workspace: the library's fixed
+    device scratch holds D (B*H*N <= NOALLOC_MAX_ROWS).  Nothing is allocated."""
+    import torch
+    B, H, N, d = _shape(q, k, v, o, dout)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _need(lse, "lse", (B, H, N), torch.float32, q.device)
+    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _need(t, name, q.shape, q.dtype, q.device)
+    _check(attn_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, causal,
+                            scale, _dtype_code(q), _stream_handle(q.device)))
     return dq, dk, dv
 
 

@@ -23,7 +23,7 @@ PROBE = os.path.join(HERE, "rate_probe")  # instruction-rate microbenchmark (an 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_unfused.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_unfused.hip", "attn_noalloc.hip"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-I" + INCLUDE, "-I" + CSRC,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-function"]
 

@@ -57,6 +57,7 @@ const char* attn_status_string(int status) {
         case ATTN_E_ALIAS: return "an output overlaps an input or another output";
         case ATTN_E_WORKSPACE: return "backward workspace missing or too small";
         case ATTN_E_HIP: return "the HIP runtime reported an error at launch";
+        case ATTN_E_TOO_LARGE: return "the problem exceeds the fixed scratch of the allocation-free entry point";
         default: return "unknown status";
     }
 }
@@ -106,9 +107,12 @@ int fwd_dense(const void* q, const void* k, const void* v, void* o, float* lse, 
     return attn::launch_fwd(p) == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 
+// from_scratch: the D buffer is the library's fixed device scratch
+// (attn_bwd_noalloc); workspace and workspace_bytes are then ignored.
 int bwd_dense(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
               void* dq, void* dk, void* dv, int B, int H, int N, int d, const uint8_t* bm, int mask_heads,
-              int causal, float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+              int causal, float scale, int dtype, void* workspace, size_t workspace_bytes, bool from_scratch,
+              void* stream) {
     int64_t rows = 0, elems = 0;
     int st = check_common(B, H, N, d, causal, scale, dtype, &rows, &elems);
     if (st != ATTN_OK) return st;
@@ -119,24 +123,32 @@ int bwd_dense(const void* q, const void* k, const void* v, const void* o, const 
         if (mb == 0) return ATTN_E_SHAPE;
     }
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_E_NULL;
-    if (!workspace) return ATTN_E_WORKSPACE;
+    if (from_scratch) workspace = nullptr;
+    else if (!workspace) return ATTN_E_WORKSPACE;
     const void* a16[] = {q, k, v, o, dout, dq, dk, dv, workspace};
     for (const void* p : a16)
         if (!aligned(p, 16)) return ATTN_E_ALIGN;
     if (!aligned(lse, 4)) return ATTN_E_ALIGN;
     const size_t ws_need = attn::bwd_workspace_bytes_rows(rows);
-    if (workspace_bytes < ws_need) return ATTN_E_WORKSPACE;
+    if (from_scratch) {
+        if (ws_need > attn::kScratchBytes) return ATTN_E_TOO_LARGE;
+    } else if (workspace_bytes < ws_need) {
+        return ATTN_E_WORKSPACE;
+    }
     const size_t tb = (size_t)elems * 2, lb = (size_t)rows * 4;
     const Range ins[] = {range_of(q, tb), range_of(k, tb), range_of(v, tb), range_of(o, tb),
                          range_of(dout, tb), range_of(lse, lb), range_of(bm, mb)};
     const Range outs[] = {range_of(dq, tb), range_of(dk, tb), range_of(dv, tb),
-                          range_of(workspace, ws_need)};
+                          range_of(workspace, from_scratch ? 0 : ws_need)};
     for (int i = 0; i < 4; ++i) {
         for (const Range& r : ins)
             if (overlap(outs[i], r)) return i == 3 ? ATTN_E_WORKSPACE : ATTN_E_ALIAS;
         for (int j = i + 1; j < 4; ++j)
             if (overlap(outs[i], outs[j])) return j == 3 ? ATTN_E_WORKSPACE : ATTN_E_ALIAS;
     }
+    // Every row's D is written by the dQ kernel before the dK/dV kernel reads
+    // it, so the scratch needs no clearing between calls.
+    if (from_scratch && attn::scratch_for_stream(stream, &workspace) != hipSuccess) return ATTN_E_HIP;
     attn::BwdParams p{q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace,
                       dense_layout(B, H, N, causal, bm, mask_heads), N, N, d, dtype, scale, stream};
     return attn::launch_bwd(p) == hipSuccess ? ATTN_OK : ATTN_E_HIP;
@@ -169,7 +181,14 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal,
              float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
     return bwd_dense(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, nullptr, 0, causal, scale, dtype, workspace,
-                     workspace_bytes, stream);
+                     workspace_bytes, false, stream);
+}
+
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal,
+                     float scale, int dtype, void* stream) {
+    return bwd_dense(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, nullptr, 0, causal, scale, dtype, nullptr, 0,
+                     true, stream);
 }
 
 int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -178,7 +197,7 @@ int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void
                          void* workspace, size_t workspace_bytes, void* stream) {
     if ((int64_t)B * H * N > 0 && !block_mask) return ATTN_E_NULL;
     return bwd_dense(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, block_mask, mask_heads, causal, scale, dtype,
-                     workspace, workspace_bytes, stream);
+                     workspace, workspace_bytes, false, stream);
 }
 
 namespace {

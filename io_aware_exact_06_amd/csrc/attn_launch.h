@@ -101,6 +101,14 @@ inline size_t unfused_workspace_bytes(int64_t B, int64_t H, int64_t N) {
     return unfused_score_bytes(B, H, N) + ((((size_t)(B * H * N) * (size_t)N * 2) + 255) & ~(size_t)255);
 }
 
+// Fixed device scratch of attn_bwd_noalloc (attn_noalloc.hip): room for the
+// per-row D terms of B*H*N <= kScratchBytes / 4 query rows.
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+
+// Device address of that scratch on the device that `stream` belongs to
+// (looked up once per device, thread-safe).
+hipError_t scratch_for_stream(void* stream, void** ptr);
+
 hipError_t launch_fwd(const FwdParams& p);
 hipError_t launch_unfused(const UnfusedParams& p);
 hipError_t launch_bwd(const BwdParams& p);

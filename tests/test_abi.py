@@ -40,7 +40,7 @@ def test_missing_library_raises_instead_of_falling_back(monkeypatch, tmp_path):
 
 
 def test_status_strings():
-    for s in range(8):
+    for s in range(9):
         assert attn.attn_status_string(s) and attn.attn_status_string(s) != "unknown status"
     assert attn.attn_status_string(99) == "unknown status"
 
@@ -223,3 +223,28 @@ def test_bench_traffic_gate():
         assert bench.measured_traffic("fwd") is None and bench.measured_traffic("bwd") is None
     finally:
         bench.TRAFFIC.update(saved)
+
+
+def bwd_noalloc(**kw):
+    a = dict(q=A, k=A + 0x100000, v=A + 0x200000, o=A + 0x300000, dout=A + 0x400000, lse=A + 0x500000,
+             dq=A + 0x600000, dk=A + 0x700000, dv=A + 0x800000, B=1, H=2, N=64, d=64, causal=0,
+             scale=0.125, dtype=1)
+    a.update(kw)
+    return attn.attn_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"],
+                                 a["B"], a["H"], a["N"], a["d"], a["causal"], a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dout=0), 1), (dict(dv=0), 1), (dict(d=80), 3), (dict(scale=float("nan")), 3),
+    (dict(dq=A + 4), 4), (dict(dq=A + 0x400000), 5), (dict(dk=A + 0x600000), 5),
+    (dict(B=1, H=1, N=attn.NOALLOC_MAX_ROWS + 1), 8),
+    (dict(B=2, H=8, N=attn.NOALLOC_MAX_ROWS // 16 + 1), 8),
+])
+def test_bwd_noalloc_rejects(kw, status):
+    """Host checks of the allocation-free backward, the size limit of its fixed
+    scratch included, all before any HIP call."""
+    assert bwd_noalloc(**kw) == status
+
+
+def test_bwd_noalloc_empty_problem_is_a_no_op():
+    assert bwd_noalloc(q=0, k=0, v=0, o=0, dout=0, lse=0, dq=0, dk=0, dv=0, N=0) == 0
