@@ -162,7 +162,19 @@ def cpu_baseline(w, inp, scale, passes, budget_s=10.0):
             "kind": "oracle",
             "sample": "%d of %d heads of the workload (N=%d, d=%d, causal=%s), %s, %.1f s"
                       % (heads, w.B * w.H, w.N, w.d, w.causal, what, total_t),
-            "cpu": platform.processor() or platform.machine()}
+            "cpu": cpu_model()}
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), else what platform reports."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def pairs_window(n, wl):
@@ -423,6 +435,50 @@ def bench_io(args):
                       "unfused": res["unfused"], "calibration_copy_bytes": 1 << 30}), flush=True)
 
 
+# Work per unmasked (query, key) pair of each pass as the kernels execute it,
+# counted from their inner loops (unmasked tiles, per lane and score element):
+#   fwd: two d-deep products (4 d MFMA FLOP); one v_exp_f32; about 4 other
+#        vector instructions (scale-and-subtract FMA, running-sum add, half a
+#        16-bit pack, half a dot2 adding the rounded weights, half a three-input
+#        maximum, plus the maximum's NaN quieting);
+#   bwd: seven d-deep products (14 d MFMA FLOP: S, dP, dQ in the dQ kernel; S,
+#        dP, dV, dK in the dK/dV kernel); two v_exp_f32 (one per kernel);
+#        about 9.5 other vector instructions (dQ kernel: FMA, dP - D, times P,
+#        half a pack; dK/dV kernel: the same plus a second half pack and two
+#        accumulator-to-VGPR copies of S and dP).
+KERNEL_WORK = {"fwd": {"mfma_flop_per_d": 4.0, "exp": 1.0, "valu": 4.0},
+               "bwd": {"mfma_flop_per_d": 14.0, "exp": 2.0, "valu": 9.5}}
+
+
+def floors(pairs, d, pass_, rates):
+    """Time floors (ms) of one pass from the measured instruction rates (each at
+    the clock its probe ran at): the matrix cores on the executed MFMA work, and
+    the vector unit on the exponentials plus the other vector instructions
+    (both issue through the vector pipe, so their times add)."""
+    kw = KERNEL_WORK[pass_]
+    cus = rates["cus"]
+    mfma_rate = rates["mfma_bf16_flop_per_clk_per_cu"] * cus * rates["mfma_mhz"] * 1e6
+    exp_rate = rates["exp_per_clk_per_cu"] * cus * rates["exp_mhz"] * 1e6
+    fma_rate = rates["fma_f32_per_clk_per_cu"] * cus * rates["fma_mhz"] * 1e6
+    t_mfma = pairs * kw["mfma_flop_per_d"] * d / mfma_rate * 1e3
+    t_exp = pairs * kw["exp"] / exp_rate * 1e3
+    t_vec = t_exp + pairs * kw["valu"] / fma_rate * 1e3
+    return {"mfma_floor_ms": round(t_mfma, 5), "exp_floor_ms": round(t_exp, 5), "vector_floor_ms": round(t_vec, 5)}
+
+
+def roof_row(prefix, pairs, d, pass_, ms, rates):
+    """Floors of a pass, the binding one and the fraction of it achieved."""
+    if not rates:
+        return {}
+    f = floors(pairs, d, pass_, rates)
+    bound = "mfma" if f["mfma_floor_ms"] >= f["vector_floor_ms"] else "vector"
+    fl = max(f["mfma_floor_ms"], f["vector_floor_ms"])
+    out = {prefix + "_" + k: v for k, v in f.items()}
+    out[prefix + "_bound"] = bound
+    out[prefix + "_frac_of_bound"] = round(fl / ms, 4)
+    return out
+
+
 def bench_configs(args):
     """Every problem configuration of the workload list, forward (and backward
     where the configuration has one), timed with HIP events on the launch
@@ -433,6 +489,7 @@ def bench_configs(args):
     from io_aware_exact_06_amd import attn
     from io_aware_exact_06_amd.inputs import WORKLOADS, default_scale, workload_inputs
 
+    rates = None if args.no_extras else run_rate_probe()  # before this process touches the GPU
     dev = torch.device("cuda:0")
     rows = []
     for idx, w in enumerate(WORKLOADS):
@@ -453,9 +510,11 @@ def bench_configs(args):
         e[1].record()
         torch.cuda.synchronize()
         f_ms = e[0].elapsed_time(e[1]) / reps
+        pairs = w.pairs_per_head() * w.B * w.H
         row = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "dtype": w.dtype,
                "causal": w.causal, "fwd_ms": round(f_ms, 5), "fwd_tflops": round(ff / f_ms / 1e9, 2),
                "fwd_pct_peak": round(100 * ff / f_ms / 1e9 / PEAK_BF16_TFLOPS, 2)}
+        row.update(roof_row("fwd", pairs, w.d, "fwd", f_ms, rates))
         if w.backward:
             do = inp["dout"].to(dev)
             dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
@@ -473,10 +532,12 @@ def bench_configs(args):
             b_ms = e[0].elapsed_time(e[1]) / args.steps
             row.update({"bwd_ms": round(b_ms, 5), "bwd_tflops": round(fb / b_ms / 1e9, 2),
                         "bwd_pct_peak": round(100 * fb / b_ms / 1e9 / PEAK_BF16_TFLOPS, 2)})
+            row.update(roof_row("bwd", pairs, w.d, "bwd", b_ms, rates))
         rows.append(row)
         del q, k, v, o, lse
     print(json.dumps({"metric": "fused attention fwd/bwd TFLOP/s per configuration", "unit": "TFLOP/s",
                       "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "peak": PEAK_BF16_TFLOPS,
+                      "rates": rates, "kernel_work_per_pair": KERNEL_WORK,
                       "data": "synthetic: the configurations' seeded inputs", "configs": rows}), flush=True)
 
 
@@ -606,15 +667,15 @@ def main():
     if bwd:
         out["bwd"] = {"median_ms": round(med(bwd_ms), 4), "min_ms": round(bwd_ms[0], 4),
                       "tflops": round(b_tf, 2), "pct_peak": round(100 * b_tf / PEAK_BF16_TFLOPS, 2)}
-    # Secondary roof: the exponentials (one per unmasked pair in the forward,
-    # one per pair in each backward kernel) at the probe's v_exp_f32 rate, on
-    # all CUs at the nominal 2.4 GHz.
+    # Floors of each pass from the measured instruction rates: the matrix cores
+    # on the executed MFMA work, the vector unit on the exponentials and other
+    # vector instructions per pair (KERNEL_WORK), each at its probe's clock.
     if rates:
-        exps_fwd = w.pairs_per_head() * w.B * w.H
-        exp_rate = rates["exp_per_clk_per_cu"] * rates["cus"] * 2.4e9
+        pairs = w.pairs_per_head() * w.B * w.H
         out["rates"] = dict(rates)
-        out["exp_bound_ms"] = {"fwd": round(exps_fwd / exp_rate * 1e3, 4),
-                               "bwd": round(2 * exps_fwd / exp_rate * 1e3, 4) if bwd else None}
+        out["floors"] = {"fwd": roof_row("fwd", pairs, w.d, "fwd", sum(fwd_ms) / len(fwd_ms), rates)}
+        if bwd:
+            out["floors"]["bwd"] = roof_row("bwd", pairs, w.d, "bwd", sum(bwd_ms) / len(bwd_ms), rates)
     fwd_only = lambda n: [attn.fwd(q, k, v, w.causal, scale, o=o, lse=lse) for _ in range(n)]
     bwd_only = lambda n: [attn.bwd(q, k, v, o, do, lse, w.causal, scale, dq=dq, dk=dk, dv=dv, workspace=ws)
                           for _ in range(n)]

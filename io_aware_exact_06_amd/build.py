@@ -4,7 +4,8 @@ Usage: python -m io_aware_exact_06_amd.build   (or __graft_entry__.build()).
 Every HIP source is compiled with packed-fp32 instructions disabled; the
 objects are linked into one shared library next to this file.  The
 instruction-rate probe (csrc/rate_probe.hip) becomes the executable
-rate_probe beside it.
+rate_probe beside it, and the dQ atomic-add probe (csrc/atomic_probe.hip) the
+executable atomic_probe.
 """
 from __future__ import annotations
 
@@ -20,6 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libattn.so")
 PROBE = os.path.join(HERE, "rate_probe")  # instruction-rate microbenchmark (an executable)
+ATOMIC_PROBE = os.path.join(HERE, "atomic_probe")  # dQ atomic-add rate microbenchmark (an executable)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -42,21 +44,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def _build_probe() -> None:
-    tmp = PROBE + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *COMMON, "-x", "hip", os.path.join(CSRC, "rate_probe.hip"), "-o", tmp]
+def _build_probe(src: str = "rate_probe.hip", out: str = None) -> None:
+    out = out or PROBE
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *COMMON, "-x", "hip", os.path.join(CSRC, src), "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError("hipcc failed for rate_probe.hip:\n" + r.stdout + r.stderr)
-    os.replace(tmp, PROBE)
+        raise RuntimeError("hipcc failed for %s:\n%s%s" % (src, r.stdout, r.stderr))
+    os.replace(tmp, out)
 
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
-        probe = ex.submit(_build_probe)
+    with cf.ThreadPoolExecutor(max_workers=len(SOURCES) + 2) as ex:
+        probes = [ex.submit(_build_probe), ex.submit(_build_probe, "atomic_probe.hip", ATOMIC_PROBE)]
         objs = list(ex.map(_compile, SOURCES))
-        probe.result()
+        for p in probes:
+            p.result()
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -21,7 +21,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWaves = 4;
 constexpr int kGroupsPerCu = 2;
-constexpr int kChains = 8;
+constexpr int kChains = 16;  // independent chains per lane: enough to cover the latency of both ops
 
 // One record per work group: shader cycles, 100 MHz ticks.  Lane 0 of wave 0
 // writes it with vector stores (a per-lane address).
