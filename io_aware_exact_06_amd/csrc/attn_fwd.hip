@@ -80,8 +80,12 @@ __device__ inline float max32(const f32x16& a, const f32x16& b) {
     return fmaxf(fmaxf(u0, u1), fmaxf(u2, u3));
 }
 
-template <class T, int D, int QB, bool BS>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+// KSPLIT = 2 (small grids): two sets of four waves share the group's query
+// rows; set h walks the key tiles first + h, first + h + 2, ... with its own
+// K/V buffers, and the two partial results merge at the end by the
+// online-softmax rule (O = a0 O0 + a1 O1, l = a0 l0 + a1 l1, a_i = 2^(c (m_i - m))).
+template <class T, int D, int QB, bool BS, int KSPLIT = 1>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads * KSPLIT, kThreads * KSPLIT),
                           amdgpu_waves_per_eu(QB == 1 ? 2 : 1, QB == 1 ? 2 : 1)))
 void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
@@ -93,14 +97,18 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     constexpr int STR = LdsStride<D>::value;   // row stride of the output staging
     constexpr int CH = D / 8;
     constexpr int BQ = kWaves * 32 * QB;       // query rows per work group
-    constexpr int SMEM = (BQ * STR > 4 * TB) ? BQ * STR : 4 * TB;
+    constexpr int NT = kThreads * KSPLIT;
+    static_assert(KSPLIT == 1 || (KSPLIT == 2 && QB == 1 && !BS), "key split: dense calls, one block per wave");
+    constexpr int SMEM = (BQ * STR > 4 * TB * KSPLIT) ? BQ * STR : 4 * TB * KSPLIT;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM];
-    uint16_t* const Kb = smem;           // K tiles: buffers 0, 1
-    uint16_t* const Vb = smem + 2 * TB;  // V tiles: buffers 0, 1
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = KSPLIT == 2 ? wave >> 2 : 0;  // key set of this wave
+    const int w = KSPLIT == 2 ? wave & 3 : wave;   // its 32-row block
     const int n32 = lane & 31, h = lane >> 5;
+    uint16_t* const Kb = smem + half * 4 * TB;  // K tiles: buffers 0, 1
+    uint16_t* const Vb = Kb + 2 * TB;           // V tiles: buffers 0, 1
 
     const int item = xcd_contiguous(blockIdx.x, gridDim.x);
     const Seq sq = resolve(L, item / ntq);
@@ -185,15 +193,16 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             while (t < tr.end && !bmrow[t >> 1]) ++t;
         return t;
     };
-    int j0 = tr.first;
+    int j0 = tr.first + half;
     if (BS)
         while (j0 < tr.end && !bmrow[j0 >> 1]) ++j0;
-    const int j1 = j0 < tr.end ? next_tile(j0) : tr.end;
+    const int j1 = j0 < tr.end ? (KSPLIT == 2 ? min(j0 + 2, tr.end) : next_tile(j0)) : tr.end;
     // Buffer parity is the tile index parity.  With a block mask the visited
     // tiles still alternate in parity: an active block is the tile pair
     // (2b, 2b+1), so the walk only ever jumps from an odd tile to an even one
     // (clipping to [tr.first, tr.end) removes tiles only at its two ends).
-    const int p0 = j0 & 1;
+    // With the key split, the buffer parity is the position in the set's walk.
+    const int p0 = KSPLIT == 2 ? 0 : j0 & 1;
 
     // Prologue: tiles j0 (K, V) and j1 (K) in flight, then the scores of j0.
     if (j0 < tr.end) {
@@ -312,7 +321,47 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         wait_dma();
     };
 
-    if constexpr (!BS) {
+    if constexpr (KSPLIT == 2) {
+        // Position k of set `half` is tile first + half + 2k, in buffers k & 1.
+        // Both sets run n0 steps (one barrier each); a set with one tile
+        // fewer ends on a bare barrier.
+        const int nt = tr.end - tr.first;
+        const int n0 = (nt + 1) >> 1, nh = (nt + 1 - half) >> 1;
+        auto tile_at = [&](int k) __attribute__((always_inline)) { return tr.first + half + 2 * k; };
+        // number of positions whose tile lies below t
+        auto pos_of = [&](int t) __attribute__((always_inline)) { return max(0, (t - tr.first - half + 1) >> 1); };
+        if (nh > 0) {
+            const int lastk = nh - 1;
+            // positions [ka, kb) of one kind, each with a successor
+            auto run = [&](int ka, int kb, auto masked_tag) __attribute__((always_inline)) {
+                int k = ka;
+                if (k < kb && (k & 1)) {
+                    step(tile_at(k), tile_at(k + 1), tile_at(k + 2), Flag<1>{}, masked_tag, Flag<true>{});
+                    ++k;
+                }
+                for (; k + 1 < kb; k += 2) {
+                    step(tile_at(k), tile_at(k + 1), tile_at(k + 2), Flag<0>{}, masked_tag, Flag<true>{});
+                    step(tile_at(k + 1), tile_at(k + 2), tile_at(k + 3), Flag<1>{}, masked_tag, Flag<true>{});
+                }
+                if (k < kb) step(tile_at(k), tile_at(k + 1), tile_at(k + 2), Flag<0>{}, masked_tag, Flag<true>{});
+            };
+            const int kff = min(pos_of(tr.full_first), lastk);
+            const int kfe = min(max(pos_of(tr.full_end), kff), lastk);
+            run(0, kff, Flag<true>{});
+            run(kff, kfe, Flag<false>{});
+            run(kfe, lastk, Flag<true>{});
+            const int last = tile_at(lastk);
+            const bool last_masked = last < tr.full_first || last >= tr.full_end;
+            if (lastk & 1) {
+                if (last_masked) step(last, tr.end, tr.end, Flag<1>{}, Flag<true>{}, Flag<false>{});
+                else step(last, tr.end, tr.end, Flag<1>{}, Flag<false>{}, Flag<false>{});
+            } else {
+                if (last_masked) step(last, tr.end, tr.end, Flag<0>{}, Flag<true>{}, Flag<false>{});
+                else step(last, tr.end, tr.end, Flag<0>{}, Flag<false>{}, Flag<false>{});
+            }
+        }
+        if (nh < n0) __syncthreads();
+    } else if constexpr (!BS) {
         // Tiles [a, b) all of one kind (masked or not), none of them the last.
         auto run = [&](int a, int b, auto masked_tag) __attribute__((always_inline)) {
             int jt = a;
@@ -385,10 +434,44 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     }
     __syncthreads();  // every wave is done with the tile buffers
 
+    if constexpr (KSPLIT == 2) {
+        // merge the second set's partial result into the first set's
+        float* xo = (float*)smem;            // [row block][DB][16][lane]: O^T of set 1
+        float* xs = xo + 4 * DB * 16 * 64;   // [row block][m, l, lh][lane]
+        if (half == 1) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) xo[((w * DB + db) * 16 + e) * 64 + lane] = oacc[0][db][e];
+            xs[(w * 3 + 0) * 64 + lane] = m[0];
+            xs[(w * 3 + 1) * 64 + lane] = l[0];
+            xs[(w * 3 + 2) * 64 + lane] = lh[0];
+        }
+        __syncthreads();
+        if (half == 0) {
+            const float m1 = xs[(w * 3 + 0) * 64 + lane];
+            const float l1 = xs[(w * 3 + 1) * 64 + lane];
+            const float lh1 = xs[(w * 3 + 2) * 64 + lane];
+            const float mm = fmaxf(m[0], m1);
+            const float a0 = m[0] == kNegInf ? 0.f : __builtin_amdgcn_exp2f((m[0] - mm) * c);
+            const float a1 = m1 == kNegInf ? 0.f : __builtin_amdgcn_exp2f((m1 - mm) * c);
+            l[0] = a0 * l[0] + a1 * l1;
+            lh[0] = a0 * lh[0] + a1 * lh1;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    oacc[0][db][e] = a0 * oacc[0][db][e] + a1 * xo[((w * DB + db) * 16 + e) * 64 + lane];
+            m[0] = mm;
+        }
+        __syncthreads();  // the merge area is the staging area below
+    }
+
     // ---- epilogue: O = O^T / l, staged through LDS for row-contiguous stores
     uint16_t* Os = smem;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
+        if (half != 0) break;
         const int qrow = wq0 + 32 * qb + n32;
         const float lt = sum_with_other_half(l[qb]);
         const float lht = sum_with_other_half(lh[qb]);
@@ -407,10 +490,24 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     }
     __syncthreads();
     uint16_t* Oh = O + sq.qrow0 * D;
-    for (int ch = tid; ch < BQ * CH; ch += kThreads) {
+    for (int ch = tid; ch < BQ * CH; ch += NT) {
         const int r = ch / CH, col = ch % CH;
         if (q0 + r < nq) *(u32x4*)(Oh + (int64_t)(q0 + r) * D + 8 * col) = *(const u32x4*)(Os + r * STR + 8 * col);
     }
+}
+
+// Compute units of the device a stream belongs to (cached per device).
+int cu_count(void* stream) {
+    static int cache[64];
+    int dev = 0;
+    if (hipStreamGetDevice((hipStream_t)stream, &dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+    if (v <= 0) {
+        int n = 0;
+        v = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+        __atomic_store_n(&cache[dev], v, __ATOMIC_RELAXED);
+    }
+    return v;
 }
 
 template <class T, int D, bool BS>
@@ -427,6 +524,15 @@ hipError_t launch(const FwdParams& p) {
     const int64_t blocks = nseq * ntq;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    // A grid that gives each CU at most one group of four waves leaves every
+    // SIMD with a single wave: split each group's keys over two wave sets
+    // instead (eight waves per group, half the walk per set).
+    if (!BS && QB == 1 && blocks <= cu_count(p.stream)) {
+        hipLaunchKernelGGL((attn_fwd_kernel<T, D, 1, false, 2>), dim3((unsigned)blocks), dim3(2 * kThreads), 0,
+                           (hipStream_t)p.stream, (const uint16_t*)p.q, (const uint16_t*)p.k,
+                           (const uint16_t*)p.v, (uint16_t*)p.o, p.lse, p.L, ntq, ascale, ascale * kLog2e, qflip);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((attn_fwd_kernel<T, D, QB, BS>), dim3((unsigned)blocks), dim3(kThreads), 0,
                        (hipStream_t)p.stream, (const uint16_t*)p.q, (const uint16_t*)p.k,
                        (const uint16_t*)p.v, (uint16_t*)p.o, p.lse, p.L, ntq, ascale,

@@ -48,6 +48,7 @@ SMALL = [
     (1, 2, 700, 128, "f16", True),
     (1, 2, 517, 64, "bf16", False),
     (1, 1, 256, 64, "f16", False),
+    (4, 64, 200, 128, "bf16", True),
 ]
 
 

@@ -65,6 +65,9 @@ SMALL = [
     (2, 1, 191, 64, "f16", True),
     (1, 2, 1000, 128, "f16", True),
     (1, 2, 517, 64, "bf16", False),
+    # more than 256 work groups of 128 rows: the path without the key split
+    (4, 64, 200, 128, "bf16", True),
+    (2, 80, 517, 64, "f16", False),
 ]
 
 
