@@ -4,8 +4,9 @@ Usage: python -m io_aware_exact_06_amd.build   (or __graft_entry__.build()).
 Every HIP source is compiled with packed-fp32 instructions disabled; the
 objects are linked into one shared library next to this file.  The
 instruction-rate probe (csrc/rate_probe.hip) becomes the executable
-rate_probe beside it, and the dQ atomic-add probe (csrc/atomic_probe.hip) the
-executable atomic_probe.
+rate_probe beside it, the dQ atomic-add probe (csrc/atomic_probe.hip) the
+executable atomic_probe, and the MFMA/vector co-issue probe
+(csrc/issue_probe.hip) the executable issue_probe.
 """
 from __future__ import annotations
 
@@ -22,6 +23,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libattn.so")
 PROBE = os.path.join(HERE, "rate_probe")  # instruction-rate microbenchmark (an executable)
 ATOMIC_PROBE = os.path.join(HERE, "atomic_probe")  # dQ atomic-add rate microbenchmark (an executable)
+ISSUE_PROBE = os.path.join(HERE, "issue_probe")  # MFMA / vector co-issue microbenchmark (an executable)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -57,7 +59,8 @@ def _build_probe(src: str = "rate_probe.hip", out: str = None) -> None:
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES) + 2) as ex:
-        probes = [ex.submit(_build_probe), ex.submit(_build_probe, "atomic_probe.hip", ATOMIC_PROBE)]
+        probes = [ex.submit(_build_probe), ex.submit(_build_probe, "atomic_probe.hip", ATOMIC_PROBE),
+                  ex.submit(_build_probe, "issue_probe.hip", ISSUE_PROBE)]
         objs = list(ex.map(_compile, SOURCES))
         for p in probes:
             p.result()
