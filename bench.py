@@ -61,9 +61,9 @@ METRIC = "fused attention fwd/bwd TFLOP/s and % MFMA peak, N=8192 d=128 causal b
 # is reported as null.
 TRAFFIC_SOURCES = ("attn_device.h", "attn_launch.h", "attn_fwd.hip", "attn_bwd.hip")
 TRAFFIC = {
-    "sha256": "4998f211dcc6df9677618c1e985d51b5af659ed3df67387df5ecafca56a07c37",
-    "fwd": 289741760,             # attn_fwd_kernel: fetch 2 x 108195.5 KiB + write 66560.0 KiB
-    "bwd": 498931552 + 422582144,  # attn_bwd_dq_kernel (2 x 210338.9 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 140802.9 + 131072.0 KiB)
+    "sha256": "0c3536ebd91d52295bd8523a7774264e87bde53625906c1100f5327a3c24e5ee",
+    "fwd": 297972637,             # attn_fwd_kernel: fetch 2 x 112220.7 KiB + write 66560.0 KiB
+    "bwd": 500739637 + 423260938,  # attn_bwd_dq_kernel (2 x 211233.5 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 141142.2 + 131072.0 KiB)
 }
 
 
