@@ -6,7 +6,9 @@ objects are linked into one shared library next to this file.  The
 instruction-rate probe (csrc/rate_probe.hip) becomes the executable
 rate_probe beside it, the dQ atomic-add probe (csrc/atomic_probe.hip) the
 executable atomic_probe, and the MFMA/vector co-issue probe
-(csrc/issue_probe.hip) the executable issue_probe.
+(csrc/issue_probe.hip) the executable issue_probe.  Before compiling, the
+generator csrc/gen_fwd_loop.py rewrites csrc/attn_fwd_loop.inc (the forward's
+hand-scheduled loop over unmasked key tiles) if its output changed.
 """
 from __future__ import annotations
 
@@ -56,7 +58,18 @@ def _build_probe(src: str = "rate_probe.hip", out: str = None) -> None:
     os.replace(tmp, out)
 
 
+def generate() -> None:
+    """Regenerate the inline-assembly include the forward kernel uses."""
+    sys.path.insert(0, CSRC)
+    try:
+        import gen_fwd_loop
+    finally:
+        sys.path.pop(0)
+    gen_fwd_loop.main(os.path.join(CSRC, "attn_fwd_loop.inc"))
+
+
 def build(verbose: bool = True) -> str:
+    generate()
     os.makedirs(BUILD_DIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES) + 2) as ex:
         probes = [ex.submit(_build_probe), ex.submit(_build_probe, "atomic_probe.hip", ATOMIC_PROBE),

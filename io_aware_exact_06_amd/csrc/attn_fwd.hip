@@ -66,6 +66,22 @@ constexpr int kBK = 64;        // key rows per tile
 #endif
 constexpr float kLazy = 8.0f;  // rescale only when the maximum grows by more than 2^8
 
+// Runs of unmasked key tiles at d = 128 go through a hand-scheduled loop
+// (attn_fwd_loop.inc, written by gen_fwd_loop.py): the same instructions and
+// accumulation order as the step below, so bitwise-equal results, with the
+// vector work spread evenly between the MFMAs and the maximum of the next
+// tile formed under this tile's P.V products.  ATTN_FWD_ASM=0 builds the
+// kernel with the C++ step only.
+#ifndef ATTN_FWD_ASM
+#define ATTN_FWD_ASM 1
+#endif
+#if ATTN_FWD_ASM
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+#include "attn_fwd_loop.inc"
+#pragma clang diagnostic pop
+#endif
+
 // Maximum of 32 values as a tree of three-input maxima (depth 4 instead of a
 // 31-long dependent chain).
 __device__ inline float max32(const f32x16& a, const f32x16& b) {
@@ -378,7 +394,38 @@ void attn_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         if (tr.end > tr.first) {
             const int last = tr.end - 1;
             run(tr.first, min(tr.full_first, last), Flag<true>{});
-            run(tr.full_first, min(tr.full_end, last), Flag<false>{});
+            int ua = tr.full_first;
+            const int ub = min(tr.full_end, last);
+#if ATTN_FWD_ASM
+            if constexpr (QB == 1 && D == 128) {
+                // Tiles [ua, bb) through the hand-scheduled loop: unmasked, each with
+                // a successor, and K(jt + 2), V(jt + 1) whole tiles (its DMA has no
+                // clamped rows).  The loop enters with S(ua) computed and K(ua + 1),
+                // V(ua) in flight, and leaves the state the step below expects.
+                const int bb = min(ub, min(tr.end, nk / kBK) - 2);
+                if (bb > ua) {
+                    const uint32_t sl = lds_addr(Kb);
+                    const uint32_t mk0 = __builtin_amdgcn_readfirstlane(sl + w * 1024);
+                    const uint32_t mv0 = mk0 + 2 * DT::BYTES;
+                    const int rg = w / DT::CG, cg = w % DT::CG;
+                    const uint64_t wofs = (uint64_t)((rg * 16 * D + cg * 32) * 2);
+                    const uint64_t kb64 = (uint64_t)(uintptr_t)Kh + (uint64_t)(ua + 2) * DT::BYTES + wofs;
+                    const uint64_t vb64 = (uint64_t)(uintptr_t)Vh + (uint64_t)(ua + 1) * DT::BYTES + wofs;
+                    // readfirstlane returns a signed int: each half goes through uint32_t,
+                    // or a low word with bit 31 set would sign-extend into the high word
+                    const uint64_t kbs = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)kb64) |
+                                         ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(kb64 >> 32)) << 32);
+                    const uint64_t vbs = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)vb64) |
+                                         ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(vb64 >> 32)) << 32);
+                    const uint32_t g[4] = {goff, goff + 4096, goff + 8192, goff + 12288};
+                    fwd_unmasked_run<T, D>(oacc[0], sacc[0][0], sacc[1][0], m[0], l[0], lh[0], qf[0], sl + kofs[0],
+                                           sl + kofs[1], sl + vofs0, sl + vofs1, g, c, (uint32_t)(ua & 1), mk0,
+                                           mk0 + DT::BYTES, mv0, mv0 + DT::BYTES, kbs, vbs, (uint32_t)(bb - ua));
+                    ua = bb;
+                }
+            }
+#endif
+            run(ua, ub, Flag<false>{});
             run(max(tr.full_end, tr.full_first), last, Flag<true>{});
             const bool last_masked = last < tr.full_first || last >= tr.full_end;
             if (last & 1) {
