@@ -59,11 +59,11 @@ METRIC = "fused attention fwd/bwd TFLOP/s and % MFMA peak, N=8192 d=128 causal b
 # code and device compile flags they were taken on, whose digest
 # (kernel_code_digest) is stored beside them; for any other code the traffic
 # is reported as null.
-TRAFFIC_SOURCES = ("attn_device.h", "attn_launch.h", "attn_fwd.hip", "attn_bwd.hip")
+TRAFFIC_SOURCES = ("attn_device.h", "attn_launch.h", "attn_fwd.hip", "attn_fwd_loop.inc", "attn_bwd.hip")
 TRAFFIC = {
-    "sha256": "0c3536ebd91d52295bd8523a7774264e87bde53625906c1100f5327a3c24e5ee",
-    "fwd": 297972637,             # attn_fwd_kernel: fetch 2 x 112220.7 KiB + write 66560.0 KiB
-    "bwd": 500739637 + 423260938,  # attn_bwd_dq_kernel (2 x 211233.5 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 141142.2 + 131072.0 KiB)
+    "sha256": "240c42e320cb53a011c84ff4e671e76b37302641cfecbfc1b9d907c4e058113d",
+    "fwd": 294461834,             # attn_fwd_kernel: fetch 2 x 110506.1 KiB + write 66560.0 KiB
+    "bwd": 500319160 + 424243167,  # attn_bwd_dq_kernel (2 x 211027.7 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 141621.5 + 131072.0 KiB)
 }
 
 
