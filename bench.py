@@ -59,7 +59,8 @@ METRIC = "fused attention fwd/bwd TFLOP/s and % MFMA peak, N=8192 d=128 causal b
 # code and device compile flags they were taken on, whose digest
 # (kernel_code_digest) is stored beside them; for any other code the traffic
 # is reported as null.
-TRAFFIC_SOURCES = ("attn_device.h", "attn_launch.h", "attn_fwd.hip", "attn_fwd_loop.inc", "attn_bwd.hip")
+TRAFFIC_SOURCES = ("attn_device.h", "attn_launch.h", "attn_fwd.hip", "attn_fwd_loop.inc", "attn_bwd.hip",
+                   "attn_dkdv_loop.inc")
 TRAFFIC = {
     "sha256": "240c42e320cb53a011c84ff4e671e76b37302641cfecbfc1b9d907c4e058113d",
     "fwd": 294461834,             # attn_fwd_kernel: fetch 2 x 110506.1 KiB + write 66560.0 KiB

@@ -295,6 +295,21 @@ constexpr int kK_BK = 128;
 constexpr int kK_BQ = 64;
 constexpr int kK_NBUF = 3;
 
+// Runs of unmasked query tiles at d = 128 go through a hand-scheduled walk
+// (attn_dkdv_loop.inc, written by gen_dkdv_loop.py): the instructions and
+// accumulation order of the tile below, so bitwise-equal results, with the
+// vector work of each block spread over two MFMA runs and LDS operands read
+// well ahead.  ATTN_DKDV_ASM=0 builds the kernel with the C++ tile only.
+#ifndef ATTN_DKDV_ASM
+#define ATTN_DKDV_ASM 1
+#endif
+#if ATTN_DKDV_ASM
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+#include "attn_dkdv_loop.inc"
+#pragma clang diagnostic pop
+#endif
+
 template <class T, int D, bool BS>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(D == 64 ? 2 : 1, 2)))
 void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -357,7 +372,7 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 
     // Tile `it` into ring buffer b: Q and dO by DMA, the row statistics into
     // registers (stored to LDS later, once the buffer's previous statistics
-    // are no longer read).
+    // are no longer read; lse is scaled by log2(e) as it is stored).
     float st_l = kPosInf, st_d = 0.f;
     auto fetch = [&](int it, int b) __attribute__((always_inline)) {
         const int r0 = it * kK_BQ;
@@ -365,13 +380,13 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         dma_tile<D, kK_BQ>(dOh, r0, nq, smem + (2 * b + 1) * TB, w, lane, goff);
         if (tid < kK_BQ) {
             const int r = r0 + tid;
-            st_l = r < nq ? lseh[r] * kLog2e : kPosInf;  // rows past the end get P = 0
+            st_l = r < nq ? lseh[r] : kPosInf;  // rows past the end get P = 0
             st_d = r < nq ? Dh[r] : 0.f;
         }
     };
     auto store_stats = [&](int b) __attribute__((always_inline)) {
         if (tid < kK_BQ) {
-            stats[b][0][tid] = st_l;
+            stats[b][0][tid] = st_l * kLog2e;
             stats[b][1][tid] = st_d;
         }
     };
@@ -555,6 +570,48 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
             }
         };
         run(tr.full_first, Flag<true>{});
+#if ATTN_DKDV_ASM
+        if constexpr (D == 128 && !BS) {
+            // Tiles [it, bb) through the hand-scheduled walk: unmasked, not the
+            // walk's first, and every boundary fetching a whole tile (it + 2 <
+            // tr.end, ending within nq).  Entry and exit are at a tile start,
+            // with the state the C++ tile and boundary leave there.
+            const int bb = min(tr.full_end, min(tr.end, nq / kK_BQ) - 2);
+            if (bb > it) {
+                const uint32_t sm = lds_addr(smem);
+                const uint32_t hi = 3 * DT::BYTES;
+                const uint32_t f4[4] = {sm + fo[0], sm + fo[1], sm + fo[0] + hi, sm + fo[1] + hi};
+                const uint32_t t4[4] = {sm + to0, sm + to1, sm + to0 + hi, sm + to1 + hi};
+                const uint32_t sta = lds_addr(&stats[0][0][0]);
+                const uint32_t g4[4] = {goff, goff + 4096, goff + 8192, goff + 12288};
+                const uint32_t mw = __builtin_amdgcn_readfirstlane(sm + w * 1024);
+                const uint32_t mq[3] = {mw, mw + 2 * DT::BYTES, mw + 4 * DT::BYTES};
+                const uint32_t md[3] = {mw + DT::BYTES, mw + 3 * DT::BYTES, mw + 5 * DT::BYTES};
+                const int rg = w / DT::CG, cg = w % DT::CG;
+                const uint64_t wofs = (uint64_t)((rg * 16 * D + cg * 32) * 2);
+                // readfirstlane returns a signed int: each half goes through uint32_t
+                auto uniform64 = [](uint64_t x) __attribute__((always_inline)) {
+                    return (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)x) |
+                           ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(x >> 32)) << 32);
+                };
+                const uint64_t t2 = (uint64_t)(it + 2);
+                const uint64_t qsrc = uniform64((uint64_t)(uintptr_t)Qh + t2 * DT::BYTES + wofs);
+                const uint64_t dosrc = uniform64((uint64_t)(uintptr_t)dOh + t2 * DT::BYTES + wofs);
+                const uint64_t lsrc = uniform64((uint64_t)(uintptr_t)lseh + t2 * kK_BQ * 4);
+                const uint64_t dsrc = uniform64((uint64_t)(uintptr_t)Dh + t2 * kK_BQ * 4);
+                const int n = bb - it;
+                dkdv_unmasked_run<T, D>(dvacc, dkacc, kf, vf, bp[1], bds[1], st_l, st_d, f4, t4, sta + 16 * h,
+                                        sta + 4 * lane, g4, 4 * lane, c, (uint32_t)w, (uint32_t)bc, mq, md, qsrc,
+                                        dosrc, lsrc, dsrc, (uint32_t)n);
+                it = bb;
+                in1 = bb + 1;
+                in2 = min(bb + 2, tr.end);
+                bc = (bc + n) % 3;
+                bn = (bn + n) % 3;
+                bpv = (bpv + n) % 3;
+            }
+        }
+#endif
         run(tr.full_end, Flag<false>{});
         run(tr.end, Flag<true>{});
         // block 1 of the last tile (now the previous buffer)

@@ -4,7 +4,8 @@
   halves must widen each half through uint32_t: the builtin returns a signed
   int, and a low word with bit 31 set would otherwise sign-extend into the
   high word (a DMA source address with its upper half all ones).
-* The committed attn_fwd_loop.inc is what gen_fwd_loop.py writes.
+* The committed attn_fwd_loop.inc and attn_dkdv_loop.inc are what their
+  generators write.
 """
 import os
 import re
@@ -28,13 +29,15 @@ def test_readfirstlane_widened_through_uint32():
     assert not bad, "readfirstlane widened to 64 bits without a uint32_t cast: %s" % bad
 
 
-def test_generated_loop_in_sync(tmp_path):
+def test_generated_loops_in_sync(tmp_path):
     sys.path.insert(0, CSRC)
     try:
+        import gen_dkdv_loop
         import gen_fwd_loop
     finally:
         sys.path.pop(0)
-    out = tmp_path / "loop.inc"
-    gen_fwd_loop.main(str(out))
-    with open(os.path.join(CSRC, "attn_fwd_loop.inc")) as fh:
-        assert fh.read() == out.read_text()
+    for gen, name in ((gen_fwd_loop, "attn_fwd_loop.inc"), (gen_dkdv_loop, "attn_dkdv_loop.inc")):
+        out = tmp_path / name
+        gen.main(str(out))
+        with open(os.path.join(CSRC, name)) as fh:
+            assert fh.read() == out.read_text(), name
