@@ -62,9 +62,9 @@ METRIC = "fused attention fwd/bwd TFLOP/s and % MFMA peak, N=8192 d=128 causal b
 TRAFFIC_SOURCES = ("attn_device.h", "attn_launch.h", "attn_fwd.hip", "attn_fwd_loop.inc", "attn_bwd.hip",
                    "attn_dkdv_loop.inc")
 TRAFFIC = {
-    "sha256": "240c42e320cb53a011c84ff4e671e76b37302641cfecbfc1b9d907c4e058113d",
-    "fwd": 294461834,             # attn_fwd_kernel: fetch 2 x 110506.1 KiB + write 66560.0 KiB
-    "bwd": 500319160 + 424243167,  # attn_bwd_dq_kernel (2 x 211027.7 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 141621.5 + 131072.0 KiB)
+    "sha256": "21c18373ac6fcd2aa33454f2caa59bd3555abda67c4b64dafa412283b4fb6a47",
+    "fwd": 295544973,             # attn_fwd_kernel: fetch 2 x 111036.2 KiB + write 66560.0 KiB
+    "bwd": 498577624 + 405529831,  # attn_bwd_dq_kernel (2 x 210179.6 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 132485.1 + 131072.0 KiB)
 }
 
 
