@@ -60,7 +60,7 @@ METRIC = "fused attention fwd/bwd TFLOP/s and % MFMA peak, N=8192 d=128 causal b
 # (kernel_code_digest) is stored beside them; for any other code the traffic
 # is reported as null.
 TRAFFIC_SOURCES = ("attn_device.h", "attn_launch.h", "attn_fwd.hip", "attn_fwd_loop.inc", "attn_bwd.hip",
-                   "attn_dkdv_loop.inc")
+                   "attn_dq_loop.inc", "attn_dkdv_loop.inc")
 TRAFFIC = {
     "sha256": "21c18373ac6fcd2aa33454f2caa59bd3555abda67c4b64dafa412283b4fb6a47",
     "fwd": 295544973,             # attn_fwd_kernel: fetch 2 x 111036.2 KiB + write 66560.0 KiB

@@ -7,9 +7,9 @@ instruction-rate probe (csrc/rate_probe.hip) becomes the executable
 rate_probe beside it, the dQ atomic-add probe (csrc/atomic_probe.hip) the
 executable atomic_probe, and the MFMA/vector co-issue probe
 (csrc/issue_probe.hip) the executable issue_probe.  Before compiling, the
-generators csrc/gen_fwd_loop.py and csrc/gen_dkdv_loop.py rewrite
-csrc/attn_fwd_loop.inc and csrc/attn_dkdv_loop.inc (the hand-scheduled loops of
-the forward and the dK/dV kernel) if their output changed.
+generators csrc/gen_fwd_loop.py, csrc/gen_dq_loop.py and csrc/gen_dkdv_loop.py
+rewrite csrc/attn_fwd_loop.inc, csrc/attn_dq_loop.inc and csrc/attn_dkdv_loop.inc
+(the hand-scheduled loops of the three kernels) if their output changed.
 """
 from __future__ import annotations
 
@@ -60,15 +60,17 @@ def _build_probe(src: str = "rate_probe.hip", out: str = None) -> None:
 
 
 def generate() -> None:
-    """Regenerate the inline-assembly includes of the forward and dK/dV kernels."""
+    """Regenerate the inline-assembly includes of the forward, dQ and dK/dV kernels."""
     sys.path.insert(0, CSRC)
     try:
         import gen_dkdv_loop
+        import gen_dq_loop
         import gen_fwd_loop
     finally:
         sys.path.pop(0)
     gen_fwd_loop.main(os.path.join(CSRC, "attn_fwd_loop.inc"))
     gen_dkdv_loop.main(os.path.join(CSRC, "attn_dkdv_loop.inc"))
+    gen_dq_loop.main(os.path.join(CSRC, "attn_dq_loop.inc"))
 
 
 def build(verbose: bool = True) -> str:

@@ -102,6 +102,21 @@ __device__ inline void store_staged(uint16_t* __restrict__ dst, const uint16_t* 
 constexpr int kQ_BQ = 128;
 constexpr int kQ_BK = 64;
 
+// Runs of unmasked key tiles at d = 128 go through a hand-scheduled walk
+// (attn_dq_loop.inc, written by gen_dq_loop.py): each accumulator sees the
+// operands and order of the step below, so bitwise-equal results, with the
+// exponentials and dS of each key block issued between the MFMAs as soon as
+// their inputs exist.  ATTN_DQ_ASM=0 builds the kernel with the C++ step only.
+#ifndef ATTN_DQ_ASM
+#define ATTN_DQ_ASM 1
+#endif
+#if ATTN_DQ_ASM
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+#include "attn_dq_loop.inc"
+#pragma clang diagnostic pop
+#endif
+
 template <class T, int D, bool BS>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -253,7 +268,37 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     };
     if constexpr (!BS) {
         for (int jt = tr.first; jt < tr.full_first; ++jt) step(jt, jt + 1, jt - tr.first & 1, Flag<true>{});
-        for (int jt = tr.full_first; jt < tr.full_end; ++jt) step(jt, jt + 1, jt - tr.first & 1, Flag<false>{});
+        int ua = tr.full_first;
+#if ATTN_DQ_ASM
+        if constexpr (D == 128) {
+            // Tiles [ua, bb) through the hand-scheduled walk: unmasked, each
+            // loading a whole next tile (jt + 1 < tr.end, ending within nk).
+            // It enters after a step's barrier (tile ua landed, nothing in
+            // flight) and leaves in the same state for tile bb.
+            const int bb = min(tr.full_end, min(tr.end, nk / kQ_BK) - 1);
+            if (bb > ua) {
+                const uint32_t sm = lds_addr(smem);
+                const uint32_t g4[4] = {goff, goff + 4096, goff + 8192, goff + 12288};
+                const uint32_t mk0 = __builtin_amdgcn_readfirstlane(sm + w * 1024);
+                const uint32_t mv0 = mk0 + 2 * DT::BYTES;
+                const int rg = w / DT::CG, cg = w % DT::CG;
+                const uint64_t wofs = (uint64_t)((rg * 16 * D + cg * 32) * 2);
+                // readfirstlane returns a signed int: each half goes through uint32_t
+                auto uniform64 = [](uint64_t x) __attribute__((always_inline)) {
+                    return (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)x) |
+                           ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(x >> 32)) << 32);
+                };
+                const uint64_t t1 = (uint64_t)(ua + 1);
+                const uint64_t ksrc = uniform64((uint64_t)(uintptr_t)Kh + t1 * DT::BYTES + wofs);
+                const uint64_t vsrc = uniform64((uint64_t)(uintptr_t)Vh + t1 * DT::BYTES + wofs);
+                dq_unmasked_run<T, D>(dqacc, qf, dof, lse2, Dq, sm + fo[0], sm + fo[1], sm + to0, sm + to1, g4, c,
+                                      (uint32_t)((ua - tr.first) & 1), mk0, mk0 + DT::BYTES, mv0, mv0 + DT::BYTES,
+                                      ksrc, vsrc, (uint32_t)(bb - ua));
+                ua = bb;
+            }
+        }
+#endif
+        for (int jt = ua; jt < tr.full_end; ++jt) step(jt, jt + 1, jt - tr.first & 1, Flag<false>{});
         for (int jt = tr.full_end; jt < tr.end; ++jt) step(jt, jt + 1, jt - tr.first & 1, Flag<true>{});
     } else {
         // The visited tiles ascend; masked ones lie before full_first or from

@@ -1,8 +1,10 @@
-"""The dK/dV kernel's hand-scheduled walk over unmasked query tiles (d = 128),
-against the fp64 oracle: whole-tensor rel-L2 of dQ, dK, dV (the backward
-acceptance measure) on shapes whose walks enter the loop at each of the three
-ring-buffer phases, run it for one tile or many, and leave it before a ragged
-last tile; plus packed sequences with sliding windows, and determinism."""
+"""The backward's hand-scheduled walks at d = 128 (the dK/dV kernel's over
+unmasked query tiles, the dQ kernel's over unmasked key tiles), against the
+fp64 oracle: whole-tensor rel-L2 of dQ, dK, dV (the backward acceptance
+measure) on shapes whose walks enter the loops at each ring-buffer phase (three
+in the dK/dV walk, two K/V buffers in the dQ walk), run them for one tile or
+many, and leave them before a ragged last tile; plus packed sequences with
+sliding windows (walks starting at odd tiles), and determinism."""
 import sys
 
 import numpy as np
@@ -29,9 +31,11 @@ def say(msg):
     (1, 3, 1500, "f16", True),
     (2, 2, 320, "bf16", False),    # walks of five tiles: the loop runs one or two
     (1, 2, 2048, "bf16", True),
+    (1, 3, 128, "f16", False),     # two key tiles: the dQ walk runs a single tile
+    (2, 2, 200, "bf16", False),    # the dQ walk runs two tiles, a ragged one follows
 ])
-def test_dkdv_loop_dense(B, H, N, dtype, causal):
-    label = "dkdv loop B%d H%d N%d %s causal=%d" % (B, H, N, dtype, causal)
+def test_bwd_loop_dense(B, H, N, dtype, causal):
+    label = "bwd loops B%d H%d N%d %s causal=%d" % (B, H, N, dtype, causal)
     say(label)
     d = 128
     inp = make_inputs(B, H, N, d, dtype, seed=N + 7 * H + causal, with_dout=True)
@@ -48,7 +52,7 @@ def test_dkdv_loop_dense(B, H, N, dtype, causal):
 
 
 @pytest.mark.parametrize("window", [(300, 0), (500, 200)])
-def test_dkdv_loop_windows(window):
+def test_bwd_loop_windows(window):
     lq = [1200, 700, 1600]
     H, d, dtype = 2, 128, "bf16"
     tq = sum(lq)
@@ -68,7 +72,7 @@ def test_dkdv_loop_windows(window):
     assert max(errs) <= GRAD_TOL, errs
 
 
-def test_dkdv_loop_deterministic():
+def test_bwd_loop_deterministic():
     inp = make_inputs(1, 4, 1024, 128, "bf16", seed=21, with_dout=True)
     q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "dout"))
     o, lse = attn.fwd(q, k, v, True, 0.09)

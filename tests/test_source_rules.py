@@ -4,8 +4,8 @@
   halves must widen each half through uint32_t: the builtin returns a signed
   int, and a low word with bit 31 set would otherwise sign-extend into the
   high word (a DMA source address with its upper half all ones).
-* The committed attn_fwd_loop.inc and attn_dkdv_loop.inc are what their
-  generators write.
+* The committed attn_fwd_loop.inc, attn_dq_loop.inc and attn_dkdv_loop.inc are
+  what their generators write.
 """
 import os
 import re
@@ -33,10 +33,12 @@ def test_generated_loops_in_sync(tmp_path):
     sys.path.insert(0, CSRC)
     try:
         import gen_dkdv_loop
+        import gen_dq_loop
         import gen_fwd_loop
     finally:
         sys.path.pop(0)
-    for gen, name in ((gen_fwd_loop, "attn_fwd_loop.inc"), (gen_dkdv_loop, "attn_dkdv_loop.inc")):
+    for gen, name in ((gen_fwd_loop, "attn_fwd_loop.inc"), (gen_dkdv_loop, "attn_dkdv_loop.inc"),
+                      (gen_dq_loop, "attn_dq_loop.inc")):
         out = tmp_path / name
         gen.main(str(out))
         with open(os.path.join(CSRC, name)) as fh:
