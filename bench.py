@@ -62,9 +62,9 @@ METRIC = "fused attention fwd/bwd TFLOP/s and % MFMA peak, N=8192 d=128 causal b
 TRAFFIC_SOURCES = ("attn_device.h", "attn_launch.h", "attn_fwd.hip", "attn_fwd_loop.inc", "attn_bwd.hip",
                    "attn_dq_loop.inc", "attn_dkdv_loop.inc")
 TRAFFIC = {
-    "sha256": "21c18373ac6fcd2aa33454f2caa59bd3555abda67c4b64dafa412283b4fb6a47",
-    "fwd": 295544973,             # attn_fwd_kernel: fetch 2 x 111036.2 KiB + write 66560.0 KiB
-    "bwd": 498577624 + 405529831,  # attn_bwd_dq_kernel (2 x 210179.6 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 132485.1 + 131072.0 KiB)
+    "sha256": "cb351679c99f7caa55aa4c1ff0ba75673f847f6bbaa9bcfbe9182cf47b16833c",
+    "fwd": 296118237,             # attn_fwd_kernel: fetch 2 x 111314.8 KiB + write 66560.0 KiB
+    "bwd": 496068844 + 405474189,  # attn_bwd_dq_kernel (2 x 208952.0 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 132456.3 + 131072.0 KiB)
 }
 
 
