@@ -81,7 +81,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * Bytes of device workspace attn_bwd needs for these sizes (0 for an empty
- * problem): the fp32 row terms D_i = <dO_i, O_i>, [B, H, N], rounded up to a
+ * problem): the fp32 row terms -D_i (D_i = <dO_i, O_i>), [B, H, N], rounded up to a
  * multiple of 256 bytes.  Returns (size_t)-1 for negative sizes.
  */
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);

@@ -163,7 +163,8 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
         dpart += dot8<T>(dof[ks], of);
     }
     const float Dq = sum_with_other_half(dpart);
-    if (h == 0 && valid) Delta[sq.qrow0 + qrow] = Dq;
+    // stored negated: the dK/dV kernel starts its dP accumulators from -D
+    if (h == 0 && valid) Delta[sq.qrow0 + qrow] = -Dq;
     const float lse2 = valid ? LSE[sq.qrow0 + qrd] * kLog2e : kPosInf;
 
     // Key tiles some row of the group sees, and those every row sees in full.
@@ -368,7 +369,7 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     constexpr int TB = DT::ELEMS;
     constexpr int SMEM = (kK_BK * STR > 2 * kK_NBUF * TB) ? kK_BK * STR : 2 * kK_NBUF * TB;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[SMEM];  // buffer b: Q tile 2b, dO tile 2b + 1
-    __shared__ __attribute__((aligned(16))) float stats[kK_NBUF][2][kK_BQ];  // [buffer][lse*log2e, D][row]
+    __shared__ __attribute__((aligned(16))) float stats[kK_NBUF][2][kK_BQ];  // [buffer][lse*log2e, -D][row]
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -382,7 +383,7 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     const uint16_t *Qh = Q + sq.qrow0 * D, *dOh = dO + sq.qrow0 * D;
     const uint16_t *Kh = K + sq.krow0 * D, *Vh = V + sq.krow0 * D;
     const float* lseh = LSE + sq.qrow0;
-    const float* Dh = Delta + sq.qrow0;
+    const float* Dh = Delta + sq.qrow0;  // -D of each row, as the dq kernel stores it
     const int krow = k0 + 32 * w + n32;
 
     // Resident K and V fragments (B operands of S = Q K^T and dP = dO V^T).
@@ -464,10 +465,16 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         u32x4 fa[2 * KS];
 #pragma unroll
         for (int i = 0; i < 2 * KS; ++i) fa[i] = rd(i);
+        // dP starts from -D of the rows this lane holds (8g + 4h + 0..3), so
+        // the products leave dP - D, the factor of dS, in the accumulator
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            s[e] = 0.f;
-            dp[e] = 0.f;
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 nd = *(const f32x4*)(&stats[b][1][32 * QBI + 8 * g + 4 * h]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                s[4 * g + r] = 0.f;
+                dp[4 * g + r] = nd[r];
+            }
         }
 #pragma unroll
         for (int i = 0; i < 2 * KS; ++i) {
@@ -495,13 +502,10 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         auto rd = [&](int i) __attribute__((always_inline)) {
             return tr_operand_dma((i & 1) ? qt_ : ot_, to0, to1, DT::tr_blk(2 * QP + ((i >> 1) & 1), i >> 2));
         };
-        // row statistics of the query rows this lane holds: 8g + 4h + (0..3)
-        f32x4 l4[4], d4[4];
+        // lse * log2(e) of the query rows this lane holds: 8g + 4h + (0..3)
+        f32x4 l4[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            l4[g] = *(const f32x4*)(&stats[b][0][32 * QC + 8 * g + 4 * h]);
-            d4[g] = *(const f32x4*)(&stats[b][1][32 * QC + 8 * g + 4 * h]);
-        }
+        for (int g = 0; g < 4; ++g) l4[g] = *(const f32x4*)(&stats[b][0][32 * QC + 8 * g + 4 * h]);
         u32x4 ta[NB];
         if (PREV) {
 #pragma unroll
@@ -521,7 +525,7 @@ void attn_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
                 if (!sq.visible(qb0 + 8 * g + 4 * h + r, krow)) pe = 0.f;
             }
             pv[e] = pe;
-            dv[e] = pe * (dp[e] - d4[g][r]);
+            dv[e] = pe * dp[e];  // dp holds dP - D (part_a)
             if (e & 1) {
                 bpo[e >> 3][(e & 7) >> 1] = pack2<T>(pv[e - 1], pv[e]);
                 bdo[e >> 3][(e & 7) >> 1] = pack2<T>(dv[e - 1], dv[e]);

@@ -1,7 +1,7 @@
 // attn_noalloc.hip -- the fixed device scratch behind attn_bwd_noalloc.
 //
 // attn_bwd needs a caller-supplied workspace for the per-row terms
-// D_i = <dO_i, O_i>, which the dQ kernel writes and the dK/dV kernel reads.
+// -D_i (D_i = <dO_i, O_i>), which the dQ kernel writes and the dK/dV kernel reads.
 // Callers that cannot allocate device memory (code under graph capture,
 // tight serving loops) use attn_bwd_noalloc instead.  Its D buffer is the
 // file-scope array below: every GPU the library runs on holds one copy of it,

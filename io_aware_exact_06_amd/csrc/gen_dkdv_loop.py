@@ -15,7 +15,7 @@ Iteration k of the loop issues
          tile), then, for odd k, the tile boundary (DMA wait, the next tile's
          row statistics into LDS, barrier, the DMA of the tile after it);
   run 2: the 16 S / dP MFMAs of block k+1 (operands read from its tile);
-and spreads the vector work of block k (P, dS and their packing, about 80
+and spreads the vector work of block k (P, dS and their packing, 64
 instructions with 16 exponentials) over both runs.  The C++ tile issues S, dP
 of a block alone and then its vector work beside the previous block's dV, dK:
 with one wave per SIMD nothing else fills the matrix cores while it waits.
@@ -28,8 +28,9 @@ Register map (physical; 512 per lane at one wave per SIMD):
   a192..a255  LDS operand ring (16 slots)
   v0..v31     S, dP of even blocks   v32..v63   S, dP of odd blocks
   v64..v79    packed P, dS of even blocks (B operands)   v80..v95 of odd blocks
-  v96..v127   lse*log2e and D rows of even blocks        v128..v159 of odd blocks
-  v160, v161  the next tile's lse and D rows as loaded by wave 0 (lse is scaled by
+  v96..v127   lse*log2e and -D rows of even blocks       v128..v159 of odd blocks
+              (the -D rows are the initial accumulators of dP: the products leave dP - D)
+  v160, v161  the next tile's lse and -D rows as loaded by wave 0 (lse is scaled by
               log2(e) when it is stored to LDS, as in the C++ boundary)
 SGPR pairs s[80:81], s[82:83], s[84:85], s[86:87]: DMA sources of the next Q
 and dO tile, and the next tile's lse and D rows.
@@ -134,7 +135,10 @@ def generate(T, D):
             reads = [("ds_read_b128", "%s%d]" % (reg, (i >> 1) & 1), imm, 4, 0)]
             dst = SDP[s_set] + (16 if i & 1 else 0)
             bop = (VF if i & 1 else KF) + 4 * (i >> 1)
-            out.append(dict(reads=reads, dst=dst, acc_agpr=False, b=ar(bop, 4), b_regs=(), first=(i >> 1) == 0))
+            # S starts from 0, dP from the -D rows of the block (so it ends as dP - D)
+            c0 = STAT[s_set] + 16 if i == 1 else None
+            out.append(dict(reads=reads, dst=dst, acc_agpr=False, b=ar(bop, 4), b_regs=(), first=(i >> 1) == 0,
+                            c0=c0))
         return out
 
     def b_mfmas(b, qp, p_set):
@@ -152,17 +156,17 @@ def generate(T, D):
         return out
 
     def v_ops(s_set, p_set):
-        """P = exp2(s c - lse log2e), dS = P (dP - D), packed as B operands (the C++ element order)."""
+        """P = exp2(s c - lse log2e), dS = P (dP - D) (the dP accumulator already holds
+        dP - D), packed as B operands (the C++ element order)."""
         sb, dpb = SDP[s_set], SDP[s_set] + 16
-        lb, db_ = STAT[s_set], STAT[s_set] + 16
+        lb = STAT[s_set]
         pb, dsb = PK[p_set], PK[p_set] + 8
         ops = []
         for e in range(16):
             g, r = e >> 2, e & 3
-            l, d = lb + 4 * g + r, db_ + 4 * g + r
+            l = lb + 4 * g + r
             ops.append(("v_fma_f32 %s, %s, %%[c], -%s" % (vr(sb + e), vr(sb + e), vr(l)), "valu", [sb + e, l], [sb + e]))
             ops.append(("v_exp_f32 %s, %s" % (vr(sb + e), vr(sb + e)), "trans", [sb + e], [sb + e]))
-            ops.append(("v_sub_f32 %s, %s, %s" % (vr(dpb + e), vr(dpb + e), vr(d)), "valu", [dpb + e, d], [dpb + e]))
             ops.append(("v_mul_f32 %s, %s, %s" % (vr(dpb + e), vr(sb + e), vr(dpb + e)), "valu", [sb + e, dpb + e], [dpb + e]))
             if e & 1:
                 q = (e & 7) >> 1
@@ -186,7 +190,7 @@ def generate(T, D):
     # ---------------------------------------------------------------- emission helpers
     slot = [0]       # next ring slot
 
-    def run_mfmas(mlist, vops, vquota, extra_reads=None, after=None):
+    def run_mfmas(mlist, vops, vquota, extra_reads=None, after=None, pre_reads=()):
         """Issue the MFMAs of mlist with their LDS reads AHEAD slots ahead and vquota[j]
         vector ops after MFMA j; extra_reads (LDS reads into other registers) are
         issued after the second MFMA, after[j] (scalar and memory instructions)
@@ -205,6 +209,8 @@ def generate(T, D):
                     dst = sl + half
                     S.lds_op("%s %s, %s offset:%d" % (op, ar(dst, nreg), addr, imm),
                              ["a%d" % r for r in range(dst, dst + nreg)])
+        for (t, dst) in pre_reads:
+            S.lds_op(t, dst)
         ahead = min(AHEAD, n)
         for j in range(ahead):
             issue(j)
@@ -227,10 +233,13 @@ def generate(T, D):
 
     def emit_mfma(M, slot_index):
         sl = RING + 4 * slot_index
-        S.lds_wait(["a%d" % r for r in range(sl, sl + 4)])
+        c0 = M.get("c0")
+        S.lds_wait(["a%d" % r for r in range(sl, sl + 4)] + (list(range(c0, c0 + 16)) if c0 is not None else []))
         reads = list(M["b_regs"]) + ([] if M["first"] or M["acc_agpr"] else list(range(M["dst"], M["dst"] + 16)))
+        if c0 is not None:
+            reads += list(range(c0, c0 + 16))
         dn = ar(M["dst"], 16) if M["acc_agpr"] else vr(M["dst"], 16)
-        c = "0" if M["first"] else dn
+        c = (vr(c0, 16) if c0 is not None else "0") if M["first"] else dn
         S.ins("%s %s, %s, %s, %s" % (mfma, dn, ar(sl, 4), M["b"], c), "mfma", reads,
               [] if M["acc_agpr"] else list(range(M["dst"], M["dst"] + 16)),
               acc=None if M["acc_agpr"] else tuple(range(M["dst"], M["dst"] + 16)))
@@ -348,7 +357,9 @@ def generate(T, D):
         ex = label("exit")
         S.raw("s_cbranch_scc1 %s" % ex, 1)
         exits.append((ex, list(rest), bpv))
-        rest = run_mfmas(a_mfmas(bn, 0, 0), rest, quotas(len(rest), 2 * KS), extra_reads=stat_reads(bn, 0, 0),
+        # the -D rows first: the run's second MFMA starts from them
+        st_rd = stat_reads(bn, 0, 0)
+        rest = run_mfmas(a_mfmas(bn, 0, 0), rest, quotas(len(rest), 2 * KS), pre_reads=st_rd[4:], extra_reads=st_rd[:4],
                          after=loads(bpv))
         for op in rest:
             emit_v(op)
