@@ -27,9 +27,10 @@ launches on (torch's current stream).
 The headline run also reports, outside the timed region, (i) the instruction
 rates of the part measured by the rate_probe executable (v_exp_f32, fp32 FMA
 and bf16 MFMA per CU per shader cycle) with the time those rates put under
-the passes' exponentials, and (ii) the shader clock sampled with rocm-smi
-while each pass runs back to back for about a second (the part lowers its
-clock under sustained load).
+the passes' exponentials, and (ii) the shader clock (rocm-smi) and the
+socket power (amd-smi) sampled while each pass runs back to back for a few
+seconds, beside the package power cap: the part lowers its clock to hold
+the cap under sustained load.
 """
 from __future__ import annotations
 
@@ -62,9 +63,9 @@ METRIC = "fused attention fwd/bwd TFLOP/s and % MFMA peak, N=8192 d=128 causal b
 TRAFFIC_SOURCES = ("attn_device.h", "attn_launch.h", "attn_fwd.hip", "attn_fwd_loop.inc", "attn_bwd.hip",
                    "attn_dq_loop.inc", "attn_dkdv_loop.inc")
 TRAFFIC = {
-    "sha256": "cb351679c99f7caa55aa4c1ff0ba75673f847f6bbaa9bcfbe9182cf47b16833c",
-    "fwd": 296118237,             # attn_fwd_kernel: fetch 2 x 111314.8 KiB + write 66560.0 KiB
-    "bwd": 496068844 + 405474189,  # attn_bwd_dq_kernel (2 x 208952.0 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 132456.3 + 131072.0 KiB)
+    "sha256": "ab71099ce87eded3f5d93911a86f0731437808765d33b2e07a8cf887ad52cfc1",
+    "fwd": 295920311,             # attn_fwd_kernel: fetch 2 x 111218.3 KiB + write 66560.0 KiB
+    "bwd": 487029136 + 405471754,  # attn_bwd_dq_kernel (2 x 204538.1 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 132455.3 + 131072.0 KiB)
 }
 
 
@@ -102,11 +103,13 @@ def run_rate_probe():
         return None
 
 
-def sample_sclk(run_for, seconds=1.2, samples=3):
-    """Shader clock (MHz) read with rocm-smi while run_for() keeps the GPU busy.
+def sample_sclk(run_for, seconds=2.5, samples=3):
+    """Shader clock (MHz, rocm-smi) and socket power (W, amd-smi) read while
+    run_for() keeps the GPU busy.
 
-    run_for(n) enqueues n passes; enough are queued for `seconds`, the clock
-    is sampled `samples` times while they run.  Returns the samples, or None.
+    run_for(n) enqueues n passes; enough are queued for `seconds`, and both are
+    sampled `samples` times while they run.  Returns (clocks, powers), each a
+    list of samples or None.
     """
     import torch
     try:
@@ -115,17 +118,34 @@ def sample_sclk(run_for, seconds=1.2, samples=3):
         torch.cuda.synchronize()
         per = (time.perf_counter() - t0) / 10
         run_for(max(10, int(seconds / max(per, 1e-5))))
-        got = []
+        clk, pwr = [], []
         for _ in range(samples):
-            time.sleep(seconds / (samples + 1))
+            time.sleep(seconds / (3 * samples + 1))
             r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
             m = re.search(r"sclk clock level:\s*\d+:\s*\((\d+)Mhz\)", r.stdout)
             if m:
-                got.append(int(m.group(1)))
+                clk.append(int(m.group(1)))
+            try:
+                r = subprocess.run(["amd-smi", "metric", "--power"], capture_output=True, text=True, timeout=20)
+                m = re.search(r"SOCKET_POWER:\s*(\d+)", r.stdout)
+                if m:
+                    pwr.append(int(m.group(1)))
+            except (OSError, subprocess.TimeoutExpired):
+                pass
         torch.cuda.synchronize()
-        return got or None
+        return clk or None, pwr or None
     except (OSError, subprocess.TimeoutExpired):
         torch.cuda.synchronize()
+        return None, None
+
+
+def power_cap_w():
+    """The package power cap (W) rocm-smi reports, or None."""
+    try:
+        r = subprocess.run(["rocm-smi", "--showmaxpower"], capture_output=True, text=True, timeout=20)
+        m = re.search(r"Max Graphics Package Power \(W\):\s*([0-9.]+)", r.stdout)
+        return float(m.group(1)) if m else None
+    except (OSError, subprocess.TimeoutExpired):
         return None
 
 
@@ -681,7 +701,10 @@ def main():
     bwd_only = lambda n: [attn.bwd(q, k, v, o, do, lse, w.causal, scale, dq=dq, dk=dk, dv=dv, workspace=ws)
                           for _ in range(n)]
     if not args.no_extras:
-        out["sclk_mhz_sustained"] = {"fwd": sample_sclk(fwd_only), "bwd": sample_sclk(bwd_only) if bwd else None}
+        fc, fp = sample_sclk(fwd_only)
+        bc, bp = sample_sclk(bwd_only) if bwd else (None, None)
+        out["sclk_mhz_sustained"] = {"fwd": fc, "bwd": bc}
+        out["socket_power_w"] = {"fwd": fp, "bwd": bp, "cap": power_cap_w()}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, scale, args.passes)
     print(json.dumps(out), flush=True)
