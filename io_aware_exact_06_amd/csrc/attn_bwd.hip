@@ -102,7 +102,7 @@ __device__ inline void store_staged(uint16_t* __restrict__ dst, const uint16_t* 
 constexpr int kQ_BQ = 128;
 constexpr int kQ_BK = 64;
 
-// Runs of unmasked key tiles at d = 128 go through a hand-scheduled walk
+// Runs of unmasked key tiles go through a hand-scheduled walk
 // (attn_dq_loop.inc, written by gen_dq_loop.py): each accumulator sees the
 // operands and order of the step below, so bitwise-equal results, with the
 // exponentials and dS of each key block issued between the MFMAs as soon as
@@ -271,7 +271,7 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
         for (int jt = tr.first; jt < tr.full_first; ++jt) step(jt, jt + 1, jt - tr.first & 1, Flag<true>{});
         int ua = tr.full_first;
 #if ATTN_DQ_ASM
-        if constexpr (D == 128) {
+        {
             // Tiles [ua, bb) through the hand-scheduled walk: unmasked, each
             // loading a whole next tile (jt + 1 < tr.end, ending within nk).
             // It enters after a step's barrier (tile ua landed, nothing in

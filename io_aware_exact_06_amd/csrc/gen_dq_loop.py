@@ -1,6 +1,6 @@
 """Generate attn_dq_loop.inc: the dQ kernel's walk over unmasked key tiles
-(d = 128, two waves per SIMD), scheduled by hand as one inline-assembly
-statement per input type.
+(d = 64 and 128, two waves per SIMD), scheduled by hand as one
+inline-assembly statement per input type and head size.
 
 What the loop computes is exactly the C++ step of attn_bwd.hip (the hotdry
 blog's section "4. 重计算（Recomputation）策略": S^T = K Q^T and dP^T = V dO^T
@@ -9,17 +9,18 @@ dQ^T += K^T dS^T).  Every accumulator sees the C++ step's operands in the
 C++ step's order, so the results are bitwise equal; only the interleave
 differs.
 
-Per tile and wave (64 keys, two key blocks kb of 32) the 48 MFMAs run as
-S(kb0), S(kb1), dP(kb0), dP(kb1), dQ(kb0), dQ(kb1).  The vector work is split
+Per tile and wave (64 keys, two key blocks kb of 32) the MFMAs (48 at d = 128,
+24 at d = 64) run as S(kb0), S(kb1), dP(kb0), dP(kb1), dQ(kb0), dQ(kb1).  The vector work is split
 by what it needs: the exponentials of kb (P) need only S(kb), the difference,
 product and packing (dS) need dP(kb) as well; each piece goes between the
 MFMAs from the first one that may issue it on, and the packed dS of kb is
 complete before the first dQ(kb) MFMA.  The C++ step issues all 32 S, dP
-MFMAs, then all the vector work, then dQ.  The eight DMA instructions of the
-next tile go one per two MFMAs over the first sixteen (bunched, they stall at
-issue).  LDS operands go through a ring of six four-register slots.
+MFMAs, then all the vector work, then dQ.  The DMA instructions of the next
+tile (eight at d = 128, four at d = 64) go one per two MFMAs (bunched, they
+stall at issue).  LDS operands go through a ring of six four-register slots.
 
-Register map (physical, two waves per SIMD: at most 256 VGPRs):
+Register map at d = 128 (physical, two waves per SIMD: at most 256 VGPRs; at
+d = 64 the same blocks, packed from v0 by regmap()):
   v0..v63    dQ^T accumulators (4 blocks of 32 head columns)
   v64..v95   S^T of the two key blocks     v96..v127  dP^T of the two key blocks
   v128..v159 Q^T fragments                 v160..v191 dO^T fragments
@@ -36,17 +37,31 @@ sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
 from gen_dkdv_loop import LdsStream  # noqa: E402
 from gen_fwd_loop import TYPES, vr  # noqa: E402
 
-HEAD_DIMS = (128,)
-ACC, SS, DP, QF, DOF, PK, RING = 0, 64, 96, 128, 160, 192, 208
+HEAD_DIMS = (64, 128)
 NSLOT = 6
 AHEAD = 5
-LSE2, DQ = 232, 233
-NREG = 234
+
+
+def regmap(D):
+    """Physical VGPR bases: dQ^T accumulators, S^T, dP^T, Q^T and dO^T fragments,
+    packed dS^T, the LDS ring, lse*log2e and D (d = 128: 0, 64, 96, 128, 160, 192,
+    208, 232, 233; d = 64: 0, 32, 64, 96, 112, 128, 144, 168, 169)."""
+    KS, DB = D // 16, D // 32
+    acc = 0
+    ss = acc + 16 * DB
+    dp = ss + 32
+    qf = dp + 32
+    dof = qf + 4 * KS
+    pk = dof + 4 * KS
+    ring = pk + 16
+    lse2 = ring + 4 * NSLOT
+    return acc, ss, dp, qf, dof, pk, ring, lse2, lse2 + 1
 
 
 def generate(T, D):
     mfma, cvt, _, _ = TYPES[T]
     KS, DB, CG = D // 16, D // 32, D // 32
+    ACC, SS, DP, QF, DOF, PK, RING, LSE2, DQ = regmap(D)
     TBB = 64 * D * 2
     PER_WAVE = (64 // 16) * CG // 4
     S = LdsStream()
@@ -198,6 +213,7 @@ SIGNATURE = ("f32x16 (&dq)[%(DB)s], const u32x4 (&qf)[%(KS)s], const u32x4 (&dof
 
 def function(T, D):
     KS, DB = D // 16, D // 32
+    ACC, SS, DP, QF, DOF, PK, RING, LSE2, DQ = regmap(D)
     PER_WAVE = (64 // 16) * (D // 32) // 4
     body = "\\n\\t".join(generate(T, D))
     outs = ['"+{v[%d:%d]}"(dq[%d])' % (ACC + 16 * i, ACC + 16 * i + 15, i) for i in range(DB)]
@@ -208,7 +224,7 @@ def function(T, D):
     ins += ['[f0] "v"(f0)', '[f1] "v"(f1)', '[t0] "v"(t0)', '[t1] "v"(t1)']
     ins += ['[g%d] "v"(g[%d])' % (i, i) for i in range(PER_WAVE)]
     ins += ['[c] "s"(c)', '[par] "s"(par)', '[mk0] "s"(mk0)', '[mk1] "s"(mk1)', '[mv0] "s"(mv0)', '[mv1] "s"(mv1)']
-    clobbers = ", ".join('"v%d"' % r for r in range(SS, RING + 4 * NSLOT) if not (QF <= r < DOF + 32))
+    clobbers = ", ".join('"v%d"' % r for r in range(SS, RING + 4 * NSLOT) if not (QF <= r < DOF + 4 * KS))
     return "\n".join([
         "template <>",
         "__device__ inline void dq_unmasked_run<%s, %d>(%s) {" % (T, D, SIGNATURE % {"DB": DB, "KS": KS}),

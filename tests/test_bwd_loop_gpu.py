@@ -1,5 +1,5 @@
-"""The backward's hand-scheduled walks at d = 128 (the dK/dV kernel's over
-unmasked query tiles, the dQ kernel's over unmasked key tiles), against the
+"""The backward's hand-scheduled walks (the dK/dV kernel's over unmasked query
+tiles at d = 128, the dQ kernel's over unmasked key tiles at d = 64 and 128), against the
 fp64 oracle: whole-tensor rel-L2 of dQ, dK, dV (the backward acceptance
 measure) on shapes whose walks enter the loops at each ring-buffer phase (three
 in the dK/dV walk, two K/V buffers in the dQ walk), run them for one tile or
@@ -24,20 +24,24 @@ def say(msg):
     sys.stdout.flush()
 
 
-@pytest.mark.parametrize("B,H,N,dtype,causal", [
-    (1, 4, 1024, "bf16", True),
-    (2, 3, 1024, "f16", False),
-    (1, 2, 777, "bf16", False),    # ragged: the last tiles go through the C++ tile
-    (1, 3, 1500, "f16", True),
-    (2, 2, 320, "bf16", False),    # walks of five tiles: the loop runs one or two
-    (1, 2, 2048, "bf16", True),
-    (1, 3, 128, "f16", False),     # two key tiles: the dQ walk runs a single tile
-    (2, 2, 200, "bf16", False),    # the dQ walk runs two tiles, a ragged one follows
+@pytest.mark.parametrize("B,H,N,d,dtype,causal", [
+    (1, 4, 1024, 128, "bf16", True),
+    (2, 3, 1024, 128, "f16", False),
+    (1, 2, 777, 128, "bf16", False),    # ragged: the last tiles go through the C++ tile
+    (1, 3, 1500, 128, "f16", True),
+    (2, 2, 320, 128, "bf16", False),    # walks of five tiles: the loop runs one or two
+    (1, 2, 2048, 128, "bf16", True),
+    (1, 3, 128, 128, "f16", False),     # two key tiles: the dQ walk runs a single tile
+    (2, 2, 200, 128, "bf16", False),    # the dQ walk runs two tiles, a ragged one follows
+    # d = 64: the dQ walk only (the dK/dV kernel keeps its C++ tile there)
+    (1, 3, 1024, 64, "f16", True),
+    (2, 2, 777, 64, "bf16", False),
+    (1, 2, 128, 64, "bf16", False),
+    (2, 3, 1500, 64, "f16", True),
 ])
-def test_bwd_loop_dense(B, H, N, dtype, causal):
-    label = "bwd loops B%d H%d N%d %s causal=%d" % (B, H, N, dtype, causal)
+def test_bwd_loop_dense(B, H, N, d, dtype, causal):
+    label = "bwd loops B%d H%d N%d d%d %s causal=%d" % (B, H, N, d, dtype, causal)
     say(label)
-    d = 128
     inp = make_inputs(B, H, N, d, dtype, seed=N + 7 * H + causal, with_dout=True)
     scale = default_scale(d)
     q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "dout"))
@@ -51,10 +55,10 @@ def test_bwd_loop_dense(B, H, N, dtype, causal):
     assert max(errs) <= GRAD_TOL, (label, errs)
 
 
-@pytest.mark.parametrize("window", [(300, 0), (500, 200)])
-def test_bwd_loop_windows(window):
+@pytest.mark.parametrize("window,d", [((300, 0), 128), ((500, 200), 128), ((500, 200), 64)])
+def test_bwd_loop_windows(window, d):
     lq = [1200, 700, 1600]
-    H, d, dtype = 2, 128, "bf16"
+    H, dtype = 2, "bf16"
     tq = sum(lq)
     a = make_inputs(1, H, tq, d, dtype, seed=sum(window) + 5, with_dout=True)
     q, k, v, do = a["q"][0], a["k"][0], a["v"][0], a["dout"][0]
