@@ -6,6 +6,8 @@
   high word (a DMA source address with its upper half all ones).
 * The committed attn_fwd_loop.inc, attn_dq_loop.inc and attn_dkdv_loop.inc are
   what their generators write.
+* In each generated loop, no path has more than 15 LDS instructions in flight
+  (lgkmcnt is a 4-bit counter), and every statement ends with none in flight.
 """
 import os
 import re
@@ -43,3 +45,56 @@ def test_generated_loops_in_sync(tmp_path):
         gen.main(str(out))
         with open(os.path.join(CSRC, name)) as fh:
             assert fh.read() == out.read_text(), name
+
+
+def lds_in_flight(lines):
+    """Upper bound of the LDS instructions in flight before each line of a
+    generated statement, over every path through its labels and branches:
+    ds_* adds one (saturating at 16), s_waitcnt lgkmcnt(k) caps the count at k, a label takes the
+    maximum over its fall-through and every branch to it (iterated to a fixed
+    point, so that backward branches count).  Returns (maximum, count at end)."""
+    at_label = {}
+    for _ in range(len(lines) + 1):
+        changed = False
+        n, live, mx = 0, True, 0
+        for line in lines:
+            op = line.split()[0] if line.split() else ""
+            if line.endswith(":"):
+                lab = line[:-1]
+                n = max(n if live else 0, at_label.get(lab, 0))
+                live = True
+                continue
+            if not live:
+                continue
+            if op.startswith("ds_"):
+                n = min(n + 1, 16)  # 16: already over the counter's range
+                mx = max(mx, n)
+            m = re.match(r"s_waitcnt\s.*lgkmcnt\((\d+)\)", line)
+            if m:
+                n = min(n, int(m.group(1)))
+            if op.startswith(("s_branch", "s_cbranch")):
+                target = line.split()[1]
+                if n > at_label.get(target, -1):
+                    at_label[target] = n
+                    changed = True
+                if op == "s_branch":
+                    live = False
+        if not changed:
+            return mx, n
+    raise AssertionError("no fixed point")
+
+
+def test_generated_loops_lds_counter():
+    sys.path.insert(0, CSRC)
+    try:
+        import gen_dkdv_loop
+        import gen_dq_loop
+        import gen_fwd_loop
+    finally:
+        sys.path.pop(0)
+    for gen in (gen_fwd_loop, gen_dq_loop, gen_dkdv_loop):
+        for T in ("BF16", "F16"):
+            for D in gen.HEAD_DIMS:
+                mx, end = lds_in_flight(gen.generate(T, D))
+                assert mx <= 15, (gen.__name__, T, D, mx)
+                assert end == 0, (gen.__name__, T, D, end)
