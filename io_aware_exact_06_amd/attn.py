@@ -16,6 +16,8 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libattn.so")
+# libattn.so with the hand-scheduled loops compiled out (tests compare the two bitwise)
+CSTEP_LIB_PATH = os.path.join(HERE, "libattn_cstep.so")
 
 ATTN_F16, ATTN_BF16 = 0, 1
 STATUS = {
@@ -42,39 +44,45 @@ def lib() -> ctypes.CDLL:
     """Open libattn.so (once).  Raises if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError("HIP library %s is missing: build it first "
-                               "(python -m io_aware_exact_06_amd.build)" % LIB_PATH)
-        L = ctypes.CDLL(LIB_PATH)
-        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-        L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
-        L.attn_fwd.restype = i
-        L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i]
-        L.attn_bwd_workspace_bytes.restype = sz
-        L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
-        L.attn_bwd.restype = i
-        L.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
-        L.attn_bwd_noalloc.restype = i
-        L.attn_status_string.argtypes = [i]
-        L.attn_status_string.restype = ctypes.c_char_p
-        L.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, vp]
-        L.attn_fwd_varlen.restype = i
-        L.attn_bwd_varlen_workspace_bytes.argtypes = [i, i]
-        L.attn_bwd_varlen_workspace_bytes.restype = sz
-        L.attn_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i,
-                                      f, i, vp, sz, vp]
-        L.attn_bwd_varlen.restype = i
-        L.attn_fwd_unfused_workspace_bytes.argtypes = [i, i, i]
-        L.attn_fwd_unfused_workspace_bytes.restype = sz
-        L.attn_fwd_unfused.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
-        L.attn_fwd_unfused.restype = i
-        L.attn_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, vp, i, i, f, i, vp]
-        L.attn_fwd_blocksparse.restype = i
-        L.attn_bwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, i, i, f, i, vp, sz,
-                                           vp]
-        L.attn_bwd_blocksparse.restype = i
-        _lib = L
+        _lib = open_library(LIB_PATH)
     return _lib
+
+
+def open_library(path: str) -> ctypes.CDLL:
+    """Open a build of the library (libattn.so or libattn_cstep.so) and declare
+    the C signatures.  Raises if it has not been built."""
+    if not os.path.exists(path):
+        raise RuntimeError("HIP library %s is missing: build it first "
+                           "(python -m io_aware_exact_06_amd.build)" % path)
+    L = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    L.attn_fwd.restype = i
+    L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i]
+    L.attn_bwd_workspace_bytes.restype = sz
+    L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    L.attn_bwd.restype = i
+    L.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    L.attn_bwd_noalloc.restype = i
+    L.attn_status_string.argtypes = [i]
+    L.attn_status_string.restype = ctypes.c_char_p
+    L.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, vp]
+    L.attn_fwd_varlen.restype = i
+    L.attn_bwd_varlen_workspace_bytes.argtypes = [i, i]
+    L.attn_bwd_varlen_workspace_bytes.restype = sz
+    L.attn_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i,
+                                  f, i, vp, sz, vp]
+    L.attn_bwd_varlen.restype = i
+    L.attn_fwd_unfused_workspace_bytes.argtypes = [i, i, i]
+    L.attn_fwd_unfused_workspace_bytes.restype = sz
+    L.attn_fwd_unfused.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    L.attn_fwd_unfused.restype = i
+    L.attn_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, vp, i, i, f, i, vp]
+    L.attn_fwd_blocksparse.restype = i
+    L.attn_bwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, i, i, f, i, vp, sz,
+                                       vp]
+    L.attn_bwd_blocksparse.restype = i
+    return L
 
 
 # ---- the C functions, same names, raw arguments --------------------------------

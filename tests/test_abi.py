@@ -26,6 +26,14 @@ def test_library_exports_every_declared_function():
         assert hasattr(L, n), n
 
 
+def test_cstep_library_exports_the_same_functions():
+    """libattn_cstep.so (the hand-scheduled loops compiled out, for the bitwise
+    GPU comparison) is the same C ABI."""
+    L = attn.open_library(attn.CSTEP_LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
 def test_missing_library_raises_instead_of_falling_back(monkeypatch, tmp_path):
     """Without the built library every entry point fails loudly: there is no
     other path that could compute attention."""
