@@ -203,6 +203,10 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     const uint32_t fo[2] = {DT::frag_lane(lane, 0), DT::frag_lane(lane, 1)};
     const uint32_t to0 = DT::tr_lane(lane, 0), to1 = DT::tr_lane(lane, 1);
 
+    // At d = 64 the register file has room for dP^T to start from -D (one
+    // value per lane, in all 16 elements), so the products leave dP^T - D;
+    // at d = 128 D is subtracted afterwards.
+    constexpr bool kNegD = (D == 64);
     // Tile jt in buffer buf; jn is the next tile visited.
     auto step = [&](int jt, int jn, int buf, auto masked_tag) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_tag)::value;
@@ -223,7 +227,7 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     s[kb][e] = 0.f;
-                    dp[kb][e] = 0.f;
+                    dp[kb][e] = kNegD ? -Dq : 0.f;
                 }
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
@@ -247,7 +251,7 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                         const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
                         if (key < klo || key > khi) p = 0.f;
                     }
-                    ds[e] = p * (dp[kb][e] - Dq);
+                    ds[e] = kNegD ? p * dp[kb][e] : p * (dp[kb][e] - Dq);
                 }
                 pack_acc_as_b<T>(ds, b[kb][0], b[kb][1]);
             }

@@ -15,7 +15,9 @@ by what it needs: the exponentials of kb (P) need only S(kb), the difference,
 product and packing (dS) need dP(kb) as well; each piece goes between the
 MFMAs from the first one that may issue it on, and the packed dS of kb is
 complete before the first dQ(kb) MFMA.  The C++ step issues all 32 S, dP
-MFMAs, then all the vector work, then dQ.  The DMA instructions of the next
+MFMAs, then all the vector work, then dQ.  At d = 64 the dP accumulators start
+from -D (16 registers filled once per statement), so dS needs no subtraction,
+as in the C++ step there.  The DMA instructions of the next
 tile (eight at d = 128, four at d = 64) go one per two MFMAs (bunched, they
 stall at issue).  LDS operands go through a ring of six four-register slots.
 
@@ -42,6 +44,12 @@ NSLOT = 6
 AHEAD = 5
 
 
+def negd_base(D):
+    """First of 16 VGPRs holding -D, the initial dP^T accumulator, at d = 64 (the
+    register file has no room for them at d = 128, where D is subtracted)."""
+    return regmap(D)[-1] + 1 if D == 64 else None
+
+
 def regmap(D):
     """Physical VGPR bases: dQ^T accumulators, S^T, dP^T, Q^T and dO^T fragments,
     packed dS^T, the LDS ring, lse*log2e and D (d = 128: 0, 64, 96, 128, 160, 192,
@@ -62,6 +70,7 @@ def generate(T, D):
     mfma, cvt, _, _ = TYPES[T]
     KS, DB, CG = D // 16, D // 32, D // 32
     ACC, SS, DP, QF, DOF, PK, RING, LSE2, DQ = regmap(D)
+    NEGD = negd_base(D)
     TBB = 64 * D * 2
     PER_WAVE = (64 // 16) * CG // 4
     S = LdsStream()
@@ -78,7 +87,7 @@ def generate(T, D):
         return (rs * CG + db) * 1024
 
     def mfmas(p):
-        """The tile's 48 MFMAs in issue order (K buffer p at p*TBB, V buffer p at (2+p)*TBB)."""
+        """The tile's MFMAs in issue order (K buffer p at p*TBB, V buffer p at (2+p)*TBB)."""
         out = []
         for kind in ("S0", "S1", "P0", "P1"):   # S(kb0), S(kb1), dP(kb0), dP(kb1)
             kb = int(kind[1])
@@ -88,13 +97,15 @@ def generate(T, D):
                 reads = [("ds_read_b128", "%%[f%d]" % (ks & 1), off, 4, 0)]
                 dst = (SS if kind[0] == "S" else DP) + 16 * kb
                 b = (QF if kind[0] == "S" else DOF) + 4 * ks
-                out.append(dict(reads=reads, dst=dst, b=b, first=ks == 0))
+                # with NEGD, dP starts from -D (so it ends as dP - D)
+                c0 = NEGD if (kind[0] == "P" and ks == 0 and NEGD is not None) else None
+                out.append(dict(reads=reads, dst=dst, b=b, first=ks == 0, c0=c0))
         for kb in range(2):                     # dQ(kb0), dQ(kb1): per db the C++ order kb, t
             for db in range(DB):
                 for t in range(2):
                     off = p * TBB + tr_blk(2 * kb + t, db)
                     reads = [("ds_read_b64_tr_b16", "%[t0]", off, 2, 0), ("ds_read_b64_tr_b16", "%[t1]", off, 2, 2)]
-                    out.append(dict(reads=reads, dst=ACC + 16 * db, b=PK + 8 * kb + 4 * t, first=False))
+                    out.append(dict(reads=reads, dst=ACC + 16 * db, b=PK + 8 * kb + 4 * t, first=False, c0=None))
         return out
 
     def p_ops(kb):
@@ -109,7 +120,8 @@ def generate(T, D):
         s, dp, pk = SS + 16 * kb, DP + 16 * kb, PK + 8 * kb
         ops = []
         for e in range(16):
-            ops.append(("v_sub_f32 %s, %s, %s" % (vr(dp + e), vr(dp + e), vr(DQ)), "valu", [dp + e], [dp + e]))
+            if NEGD is None:  # else the accumulator already holds dP - D
+                ops.append(("v_sub_f32 %s, %s, %s" % (vr(dp + e), vr(dp + e), vr(DQ)), "valu", [dp + e], [dp + e]))
             ops.append(("v_mul_f32 %s, %s, %s" % (vr(dp + e), vr(s + e), vr(dp + e)), "valu", [s + e, dp + e], [dp + e]))
             if e & 1:
                 d = pk + 4 * (e >> 3) + ((e & 7) >> 1)
@@ -122,6 +134,9 @@ def generate(T, D):
         dst = list(range(M["dst"], M["dst"] + 16))
         reads = list(range(M["b"], M["b"] + 4)) + ([] if M["first"] else dst)
         c = "0" if M["first"] else vr(M["dst"], 16)
+        if M["c0"] is not None:
+            reads += list(range(M["c0"], M["c0"] + 16))
+            c = vr(M["c0"], 16)
         S.ins("%s %s, %s, %s, %s" % (mfma, vr(M["dst"], 16), vr(sl, 4), vr(M["b"], 4), c), "mfma", reads, dst,
               acc=tuple(dst))
 
@@ -191,6 +206,10 @@ def generate(T, D):
         S.raw("s_addc_u32 s83, s83, 0", 4)
 
     S.nop(24)
+    if NEGD is not None:
+        # -D in all 16 elements (a sign flip, as the C++ negation)
+        for e in range(16):
+            S.ins("v_xor_b32 %s, 0x80000000, %s" % (vr(NEGD + e), vr(DQ)), "valu", [DQ], [NEGD + e])
     S.raw("s_cmp_eq_u32 %[par], 0")
     S.raw("s_cbranch_scc0 L_t1_%=")
     for p in (0, 1):
@@ -224,7 +243,9 @@ def function(T, D):
     ins += ['[f0] "v"(f0)', '[f1] "v"(f1)', '[t0] "v"(t0)', '[t1] "v"(t1)']
     ins += ['[g%d] "v"(g[%d])' % (i, i) for i in range(PER_WAVE)]
     ins += ['[c] "s"(c)', '[par] "s"(par)', '[mk0] "s"(mk0)', '[mk1] "s"(mk1)', '[mv0] "s"(mv0)', '[mv1] "s"(mv1)']
-    clobbers = ", ".join('"v%d"' % r for r in range(SS, RING + 4 * NSLOT) if not (QF <= r < DOF + 4 * KS))
+    negd = [] if negd_base(D) is None else list(range(negd_base(D), negd_base(D) + 16))
+    clobbers = ", ".join('"v%d"' % r for r in list(range(SS, RING + 4 * NSLOT)) + negd
+                         if not (QF <= r < DOF + 4 * KS))
     return "\n".join([
         "template <>",
         "__device__ inline void dq_unmasked_run<%s, %d>(%s) {" % (T, D, SIGNATURE % {"DB": DB, "KS": KS}),
