@@ -439,6 +439,7 @@ HEADER = """// attn_dkdv_loop.inc -- generated by gen_dkdv_loop.py (run by the b
 // statistics read and write addresses; g: DMA lane offsets; so: this lane's
 // statistics load offset; mq / md: DMA LDS destinations of the Q and dO tiles
 // of the three buffers for this wave.
+// n >= 1: the statement counts tiles down to zero, so a count of 0 would not end.
 """
 
 

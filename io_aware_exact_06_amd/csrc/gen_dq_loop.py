@@ -268,6 +268,7 @@ HEADER = """// attn_dq_loop.inc -- generated by gen_dq_loop.py (run by the build
 // addresses (buffer 0); g: DMA lane offsets; mk / mv: DMA LDS destinations of
 // the K and V buffers for this wave; lse2 = lse * log2(e) and dqs = D of this
 // lane's query row; c = scale * log2(e).
+// n >= 1: the statement counts tiles down to zero, so a count of 0 would not end.
 """
 
 

@@ -419,6 +419,7 @@ HEADER = """// attn_fwd_loop.inc -- generated by gen_fwd_loop.py (run by the bui
 // Inputs: k0 / k1 / v0 / v1 LDS read addresses (buffer 0), g the DMA lane
 // offsets of the wave's blocks, mk / mv the DMA LDS destinations of the two
 // K and V buffers for this wave, c = scale * log2(e) (non-negative).
+// n >= 1: the statement counts tiles down to zero, so a count of 0 would not end.
 """
 
 
