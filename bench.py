@@ -63,9 +63,9 @@ METRIC = "fused attention fwd/bwd TFLOP/s and % MFMA peak, N=8192 d=128 causal b
 TRAFFIC_SOURCES = ("attn_device.h", "attn_launch.h", "attn_fwd.hip", "attn_fwd_loop.inc", "attn_bwd.hip",
                    "attn_dq_loop.inc", "attn_dkdv_loop.inc")
 TRAFFIC = {
-    "sha256": "d2ff42e3436c89a982b8d4edf14a5809ec0c2f4bb16c2f4ddb27b9ee0cf2f461",
-    "fwd": 295498326,             # attn_fwd_kernel: fetch 2 x 111011.8 KiB + write 66560.0 KiB
-    "bwd": 484689520 + 405445046,  # attn_bwd_dq_kernel (2 x 203394.9 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 132441.8 + 131072.0 KiB)
+    "sha256": "6c3fc31cc01076671adc2f4cc04dfa0c5d142f7f55dd49a182381f431d6d93a6",
+    "fwd": 295054720,             # attn_fwd_kernel: fetch 2 x 110795.4 KiB + write 66560.0 KiB
+    "bwd": 488180719 + 405501517,  # attn_bwd_dq_kernel (2 x 205100.1 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 132469.6 + 131072.0 KiB)
 }
 
 
