@@ -58,6 +58,9 @@ STAT = (96, 128)     # lse*log2e rows at +0 (four f32x4), D rows at +16
 STL, STD = 160, 161
 TMP = 162
 NSLOT = 16
+# the read issued after MFMA j fills slot (j + AHEAD) % NSLOT, which must not be
+# the slot of MFMA j or of any MFMA still waiting for its operand
+assert AHEAD < NSLOT
 
 
 def ar(a, n=1):

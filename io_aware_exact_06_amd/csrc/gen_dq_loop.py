@@ -42,6 +42,9 @@ from gen_fwd_loop import TYPES, vr  # noqa: E402
 HEAD_DIMS = (64, 128)
 NSLOT = 6
 AHEAD = 5
+# the read issued after MFMA j fills slot (j + AHEAD) % NSLOT, which must not be
+# the slot of MFMA j or of any MFMA still waiting for its operand
+assert AHEAD < NSLOT
 
 
 def negd_base(D):

@@ -50,6 +50,10 @@ TYPES = {"BF16": ("v_mfma_f32_32x32x16_bf16", "v_cvt_pk_bf16_f32", "v_dot2c_f32_
 HEAD_DIMS = (128,)   # d = 64 measured slower with this schedule on causal workloads
 
 AHEAD = 6            # LDS operand reads in flight ahead of their MFMA
+RING_SLOTS = 8       # the ring v176..v207
+# the read issued after MFMA i fills slot (i + AHEAD) % RING_SLOTS, which must not be
+# the slot of MFMA i or of any MFMA still waiting for its operand
+assert AHEAD < RING_SLOTS
 O0, SB, Q0, P0, R0 = 0, (64, 96), 128, 160, 176
 VM, VL, VLH, VMC = 208, 209, 210, 211
 MXA, MXB, MX, SWP, TS, ALPHA, MNEW = 212, 213, 214, 215, 216, 217, 218
@@ -290,7 +294,7 @@ def generate(T, D):
 
         def reads(i):
             if i < NM:
-                slot = R0 + 4 * (i % 8)
+                slot = R0 + 4 * (i % RING_SLOTS)
                 for k, (op, addr, off, n) in enumerate(L[i]["reads"]):
                     dst = slot + (2 * k if n == 2 else 0)
                     S.ins("%s %s, %s offset:%d" % (op, vr(dst, n), addr, off), "ds", [], list(range(dst, dst + n)))
@@ -313,7 +317,7 @@ def generate(T, D):
         for i, M in enumerate(L):
             later = sum(len(L[k]["reads"]) for k in range(i + 1, min(i + AHEAD, NM)))
             S.raw("s_waitcnt lgkmcnt(%d)" % min(later, 15), 1)
-            slot = R0 + 4 * (i % 8)
+            slot = R0 + 4 * (i % RING_SLOTS)
             dst = list(range(M["dst"], M["dst"] + 16))
             rd = list(range(slot, slot + 4)) + list(range(M["b"], M["b"] + 4)) + ([] if M["first"] else dst)
             S.ins("%s %s, %s, %s, %s" % (mfma, vr(M["dst"], 16), vr(slot, 4), vr(M["b"], 4),
