@@ -203,10 +203,6 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     const uint32_t fo[2] = {DT::frag_lane(lane, 0), DT::frag_lane(lane, 1)};
     const uint32_t to0 = DT::tr_lane(lane, 0), to1 = DT::tr_lane(lane, 1);
 
-    // At d = 64 the register file has room for dP^T to start from -D (one
-    // value per lane, in all 16 elements), so the products leave dP^T - D;
-    // at d = 128 D is subtracted afterwards.
-    constexpr bool kNegD = (D == 64);
     // Tile jt in buffer buf; jn is the next tile visited.
     auto step = [&](int jt, int jn, int buf, auto masked_tag) __attribute__((always_inline)) {
         constexpr bool MASKED = decltype(masked_tag)::value;
@@ -227,7 +223,7 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     s[kb][e] = 0.f;
-                    dp[kb][e] = kNegD ? -Dq : 0.f;
+                    dp[kb][e] = -Dq;  // dP^T starts from -D: the products leave dP^T - D
                 }
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
@@ -238,7 +234,7 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
             }
             sched_reads_ahead<4, 2 * KB * KS, 1>();
             prio_normal();
-            // ---- P^T = exp(scale s - lse), dS^T = P^T o (dP^T - D)
+            // ---- P^T = exp(scale s - lse), dS^T = P^T o (dP^T - D), dP^T - D already in dp
             const int klo = sq.key_lo(qrow), khi = min(sq.key_hi(qrow), nk - 1);
             u32x4 b[KB][2];
 #pragma unroll
@@ -251,7 +247,7 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                         const int key = k0 + kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
                         if (key < klo || key > khi) p = 0.f;
                     }
-                    ds[e] = kNegD ? p * dp[kb][e] : p * (dp[kb][e] - Dq);
+                    ds[e] = p * dp[kb][e];
                 }
                 pack_acc_as_b<T>(ds, b[kb][0], b[kb][1]);
             }
@@ -283,7 +279,6 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
             const int bb = min(tr.full_end, min(tr.end, nk / kQ_BK) - 1);
             if (bb > ua) {
                 const uint32_t sm = lds_addr(smem);
-                const uint32_t g4[4] = {goff, goff + 4096, goff + 8192, goff + 12288};
                 const uint32_t mk0 = __builtin_amdgcn_readfirstlane(sm + w * 1024);
                 const uint32_t mv0 = mk0 + 2 * DT::BYTES;
                 const int rg = w / DT::CG, cg = w % DT::CG;
@@ -296,7 +291,7 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                 const uint64_t t1 = (uint64_t)(ua + 1);
                 const uint64_t ksrc = uniform64((uint64_t)(uintptr_t)Kh + t1 * DT::BYTES + wofs);
                 const uint64_t vsrc = uniform64((uint64_t)(uintptr_t)Vh + t1 * DT::BYTES + wofs);
-                dq_unmasked_run<T, D>(dqacc, qf, dof, lse2, Dq, sm + fo[0], sm + fo[1], sm + to0, sm + to1, g4, c,
+                dq_unmasked_run<T, D>(dqacc, qf, dof, lse2, Dq, sm + fo[0], sm + fo[1], sm + to0, sm + to1, goff, c,
                                       (uint32_t)((ua - tr.first) & 1), mk0, mk0 + DT::BYTES, mv0, mv0 + DT::BYTES,
                                       ksrc, vsrc, (uint32_t)(bb - ua));
                 ua = bb;

@@ -15,11 +15,13 @@ by what it needs: the exponentials of kb (P) need only S(kb), the difference,
 product and packing (dS) need dP(kb) as well; each piece goes between the
 MFMAs from the first one that may issue it on, and the packed dS of kb is
 complete before the first dQ(kb) MFMA.  The C++ step issues all 32 S, dP
-MFMAs, then all the vector work, then dQ.  At d = 64 the dP accumulators start
-from -D (16 registers filled once per statement), so dS needs no subtraction,
-as in the C++ step there.  The DMA instructions of the next
-tile (eight at d = 128, four at d = 64) go one per two MFMAs (bunched, they
-stall at issue).  LDS operands go through a ring of six four-register slots.
+MFMAs, then all the vector work, then dQ.  The dP accumulators start from -D
+(16 registers filled once per statement), so dS needs no subtraction, as in
+the C++ step.  The DMA instructions of the next tile (eight at d = 128, four
+at d = 64) go one per two MFMAs (bunched, they stall at issue); one lane-offset
+register serves all of them, the scalar source stepping 4096 bytes between
+blocks.  LDS operands go through a ring of four four-register slots, read
+three MFMAs ahead (the register file has no room for more at d = 128).
 
 Register map at d = 128 (physical, two waves per SIMD: at most 256 VGPRs; at
 d = 64 the same blocks, packed from v0 by regmap()):
@@ -27,7 +29,8 @@ d = 64 the same blocks, packed from v0 by regmap()):
   v64..v95   S^T of the two key blocks     v96..v127  dP^T of the two key blocks
   v128..v159 Q^T fragments                 v160..v191 dO^T fragments
   v192..v207 packed dS^T of the two key blocks (B operands of the dQ MFMAs)
-  v208..v231 LDS operand ring (6 slots)    v232, v233 lse*log2e and D of the row
+  v208..v223 LDS operand ring (4 slots)    v224, v225 lse*log2e and D of the row
+  v226..v241 -D (the first C operand of each dP^T chain)
 SGPR pairs s[80:81], s[82:83]: DMA sources of the next K and V tile.
 
 Run: python gen_dq_loop.py <output.inc>   (the build runs it before compiling)
@@ -40,23 +43,18 @@ from gen_dkdv_loop import LdsStream  # noqa: E402
 from gen_fwd_loop import TYPES, vr  # noqa: E402
 
 HEAD_DIMS = (64, 128)
-NSLOT = 6
-AHEAD = 5
+NSLOT = 4            # the LDS operand ring (four registers a slot)
+AHEAD = 3            # MFMAs whose operands are read ahead
 # the read issued after MFMA j fills slot (j + AHEAD) % NSLOT, which must not be
 # the slot of MFMA j or of any MFMA still waiting for its operand
 assert AHEAD < NSLOT
 
 
-def negd_base(D):
-    """First of 16 VGPRs holding -D, the initial dP^T accumulator, at d = 64 (the
-    register file has no room for them at d = 128, where D is subtracted)."""
-    return regmap(D)[-1] + 1 if D == 64 else None
-
-
 def regmap(D):
     """Physical VGPR bases: dQ^T accumulators, S^T, dP^T, Q^T and dO^T fragments,
-    packed dS^T, the LDS ring, lse*log2e and D (d = 128: 0, 64, 96, 128, 160, 192,
-    208, 232, 233; d = 64: 0, 32, 64, 96, 112, 128, 144, 168, 169)."""
+    packed dS^T, the LDS ring, lse*log2e, D and the 16 registers holding -D
+    (d = 128: 0, 64, 96, 128, 160, 192, 208, 224, 225, 226; d = 64: 0, 32, 64,
+    96, 112, 128, 144, 160, 161, 162)."""
     KS, DB = D // 16, D // 32
     acc = 0
     ss = acc + 16 * DB
@@ -66,14 +64,13 @@ def regmap(D):
     pk = dof + 4 * KS
     ring = pk + 16
     lse2 = ring + 4 * NSLOT
-    return acc, ss, dp, qf, dof, pk, ring, lse2, lse2 + 1
+    return acc, ss, dp, qf, dof, pk, ring, lse2, lse2 + 1, lse2 + 2
 
 
 def generate(T, D):
     mfma, cvt, _, _ = TYPES[T]
     KS, DB, CG = D // 16, D // 32, D // 32
-    ACC, SS, DP, QF, DOF, PK, RING, LSE2, DQ = regmap(D)
-    NEGD = negd_base(D)
+    ACC, SS, DP, QF, DOF, PK, RING, LSE2, DQ, NEGD = regmap(D)
     TBB = 64 * D * 2
     PER_WAVE = (64 // 16) * CG // 4
     S = LdsStream()
@@ -100,8 +97,8 @@ def generate(T, D):
                 reads = [("ds_read_b128", "%%[f%d]" % (ks & 1), off, 4, 0)]
                 dst = (SS if kind[0] == "S" else DP) + 16 * kb
                 b = (QF if kind[0] == "S" else DOF) + 4 * ks
-                # with NEGD, dP starts from -D (so it ends as dP - D)
-                c0 = NEGD if (kind[0] == "P" and ks == 0 and NEGD is not None) else None
+                # dP starts from -D (so it ends as dP - D)
+                c0 = NEGD if (kind[0] == "P" and ks == 0) else None
                 out.append(dict(reads=reads, dst=dst, b=b, first=ks == 0, c0=c0))
         for kb in range(2):                     # dQ(kb0), dQ(kb1): per db the C++ order kb, t
             for db in range(DB):
@@ -122,9 +119,7 @@ def generate(T, D):
     def ds_ops(kb):
         s, dp, pk = SS + 16 * kb, DP + 16 * kb, PK + 8 * kb
         ops = []
-        for e in range(16):
-            if NEGD is None:  # else the accumulator already holds dP - D
-                ops.append(("v_sub_f32 %s, %s, %s" % (vr(dp + e), vr(dp + e), vr(DQ)), "valu", [dp + e], [dp + e]))
+        for e in range(16):  # the accumulator already holds dP - D
             ops.append(("v_mul_f32 %s, %s, %s" % (vr(dp + e), vr(s + e), vr(dp + e)), "valu", [s + e, dp + e], [dp + e]))
             if e & 1:
                 d = pk + 4 * (e >> 3) + ((e & 7) >> 1)
@@ -152,9 +147,13 @@ def generate(T, D):
         kv = i >= PER_WAVE
         i %= PER_WAVE
         m0 = "%%[mv%d]" % (1 - p) if kv else "%%[mk%d]" % (1 - p)
+        lo = 82 if kv else 80
+        if i:  # the source of block i is 4096 bytes past block i - 1's (one lane-offset VGPR for all)
+            S.raw("s_add_u32 s%d, s%d, 4096" % (lo, lo), 1)
+            S.raw("s_addc_u32 s%d, s%d, 0" % (lo + 1, lo + 1), 1)
         S.raw("s_add_u32 m0, %s, %d" % (m0, 4096 * i), 1)
         S.nop(1)
-        S.raw("global_load_lds_dwordx4 %%[g%d], %s" % (i, "s[82:83]" if kv else "s[80:81]"), 1)
+        S.raw("global_load_lds_dwordx4 %%[g], s[%d:%d]" % (lo, lo + 1), 1)
 
     def tile(p):
         ML = mfmas(p)
@@ -203,16 +202,16 @@ def generate(T, D):
         # the next tile has landed for this wave; every wave is done with this one
         S.raw("s_waitcnt vmcnt(0)", 1)
         S.raw("s_barrier", 1)
-        S.raw("s_add_u32 s80, s80, %d" % TBB)
+        back = 4096 * (PER_WAVE - 1)  # the DMA stepped the sources this far inside the tile
+        S.raw("s_add_u32 s80, s80, %d" % (TBB - back))
         S.raw("s_addc_u32 s81, s81, 0")
-        S.raw("s_add_u32 s82, s82, %d" % TBB)
+        S.raw("s_add_u32 s82, s82, %d" % (TBB - back))
         S.raw("s_addc_u32 s83, s83, 0", 4)
 
     S.nop(24)
-    if NEGD is not None:
-        # -D in all 16 elements (a sign flip, as the C++ negation)
-        for e in range(16):
-            S.ins("v_xor_b32 %s, 0x80000000, %s" % (vr(NEGD + e), vr(DQ)), "valu", [DQ], [NEGD + e])
+    # -D in all 16 elements (a sign flip, as the C++ negation)
+    for e in range(16):
+        S.ins("v_xor_b32 %s, 0x80000000, %s" % (vr(NEGD + e), vr(DQ)), "valu", [DQ], [NEGD + e])
     S.raw("s_cmp_eq_u32 %[par], 0")
     S.raw("s_cbranch_scc0 L_t1_%=")
     for p in (0, 1):
@@ -229,14 +228,13 @@ def generate(T, D):
 
 
 SIGNATURE = ("f32x16 (&dq)[%(DB)s], const u32x4 (&qf)[%(KS)s], const u32x4 (&dof)[%(KS)s], float lse2, float dqs, "
-             "uint32_t f0, uint32_t f1, uint32_t t0, uint32_t t1, const uint32_t (&g)[4], float c, uint32_t par, "
+             "uint32_t f0, uint32_t f1, uint32_t t0, uint32_t t1, uint32_t g, float c, uint32_t par, "
              "uint32_t mk0, uint32_t mk1, uint32_t mv0, uint32_t mv1, uint64_t ksrc, uint64_t vsrc, uint32_t n")
 
 
 def function(T, D):
     KS, DB = D // 16, D // 32
-    ACC, SS, DP, QF, DOF, PK, RING, LSE2, DQ = regmap(D)
-    PER_WAVE = (64 // 16) * (D // 32) // 4
+    ACC, SS, DP, QF, DOF, PK, RING, LSE2, DQ, NEGD = regmap(D)
     body = "\\n\\t".join(generate(T, D))
     outs = ['"+{v[%d:%d]}"(dq[%d])' % (ACC + 16 * i, ACC + 16 * i + 15, i) for i in range(DB)]
     outs += ['[n] "+s"(n)', '"+{s[80:81]}"(ksrc)', '"+{s[82:83]}"(vsrc)']
@@ -244,9 +242,9 @@ def function(T, D):
     ins += ['"{v[%d:%d]}"(dof[%d])' % (DOF + 4 * i, DOF + 4 * i + 3, i) for i in range(KS)]
     ins += ['"{v%d}"(lse2)' % LSE2, '"{v%d}"(dqs)' % DQ]
     ins += ['[f0] "v"(f0)', '[f1] "v"(f1)', '[t0] "v"(t0)', '[t1] "v"(t1)']
-    ins += ['[g%d] "v"(g[%d])' % (i, i) for i in range(PER_WAVE)]
+    ins += ['[g] "v"(g)']
     ins += ['[c] "s"(c)', '[par] "s"(par)', '[mk0] "s"(mk0)', '[mk1] "s"(mk1)', '[mv0] "s"(mv0)', '[mv1] "s"(mv1)']
-    negd = [] if negd_base(D) is None else list(range(negd_base(D), negd_base(D) + 16))
+    negd = list(range(NEGD, NEGD + 16))
     clobbers = ", ".join('"v%d"' % r for r in list(range(SS, RING + 4 * NSLOT)) + negd
                          if not (QF <= r < DOF + 4 * KS))
     return "\n".join([
@@ -268,7 +266,7 @@ HEADER = """// attn_dq_loop.inc -- generated by gen_dq_loop.py (run by the build
 // wave's block offset).  Each tile loads the next into the other buffers,
 // computes S^T, dP^T, P^T, dS^T and dQ^T += K^T dS^T, waits for the load and
 // ends on a barrier, as the C++ step does.  f0 / f1 / t0 / t1: LDS read
-// addresses (buffer 0); g: DMA lane offsets; mk / mv: DMA LDS destinations of
+// addresses (buffer 0); g: this lane's DMA offset within a block; mk / mv: DMA LDS destinations of
 // the K and V buffers for this wave; lse2 = lse * log2(e) and dqs = D of this
 // lane's query row; c = scale * log2(e).
 // n >= 1: the statement counts tiles down to zero, so a count of 0 would not end.
