@@ -63,9 +63,9 @@ METRIC = "fused attention fwd/bwd TFLOP/s and % MFMA peak, N=8192 d=128 causal b
 TRAFFIC_SOURCES = ("attn_device.h", "attn_launch.h", "attn_fwd.hip", "attn_fwd_loop.inc", "attn_bwd.hip",
                    "attn_dq_loop.inc", "attn_dkdv_loop.inc")
 TRAFFIC = {
-    "sha256": "6c3fc31cc01076671adc2f4cc04dfa0c5d142f7f55dd49a182381f431d6d93a6",
-    "fwd": 295054720,             # attn_fwd_kernel: fetch 2 x 110795.4 KiB + write 66560.0 KiB
-    "bwd": 488180719 + 405501517,  # attn_bwd_dq_kernel (2 x 205100.1 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 132469.6 + 131072.0 KiB)
+    "sha256": "6701e0780a1bf1c66278d61609f855b02c80a01a216633ac343ec58223d26cbe",
+    "fwd": 302919846,             # attn_fwd_kernel: fetch 2 x 114636.2 KiB + write 66560.0 KiB
+    "bwd": 481490598 + 405429900,  # attn_bwd_dq_kernel (2 x 201833.6 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 132434.9 + 131072.0 KiB)
 }
 
 
