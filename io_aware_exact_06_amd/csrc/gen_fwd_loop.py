@@ -47,7 +47,8 @@ import sys
 
 TYPES = {"BF16": ("v_mfma_f32_32x32x16_bf16", "v_cvt_pk_bf16_f32", "v_dot2c_f32_bf16", "0x3f803f80"),
          "F16": ("v_mfma_f32_32x32x16_f16", "v_cvt_pk_f16_f32", "v_dot2c_f32_f16", "0x3c003c00")}
-HEAD_DIMS = (128,)   # d = 64 measured slower with this schedule on causal workloads
+HEAD_DIMS = (128,)   # at d = 64 this schedule (bitwise equal) measured 1-2% faster without a causal mask
+                     # and 4.4% slower with one (B1 H32 N8192), so d = 64 keeps the C++ step
 
 AHEAD = 6            # LDS operand reads in flight ahead of their MFMA
 RING_SLOTS = 8       # the ring v176..v207
