@@ -64,8 +64,8 @@ TRAFFIC_SOURCES = ("attn_device.h", "attn_launch.h", "attn_fwd.hip", "attn_fwd_l
                    "attn_dq_loop.inc", "attn_dkdv_loop.inc")
 TRAFFIC = {
     "sha256": "6701e0780a1bf1c66278d61609f855b02c80a01a216633ac343ec58223d26cbe",
-    "fwd": 302919846,             # attn_fwd_kernel: fetch 2 x 114636.2 KiB + write 66560.0 KiB
-    "bwd": 481490598 + 405429900,  # attn_bwd_dq_kernel (2 x 201833.6 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 132434.9 + 131072.0 KiB)
+    "fwd": 295856551,             # attn_fwd_kernel: fetch 2 x 111187.1 KiB + write 66560.0 KiB
+    "bwd": 488129917 + 405581125,  # attn_bwd_dq_kernel (2 x 205075.5 + 66560.0 KiB) + attn_bwd_dkdv_kernel (2 x 132508.7 + 131072.0 KiB)
 }
 
 
@@ -464,11 +464,11 @@ def bench_io(args):
 #        maximum, plus the maximum's NaN quieting);
 #   bwd: seven d-deep products (14 d MFMA FLOP: S, dP, dQ in the dQ kernel; S,
 #        dP, dV, dK in the dK/dV kernel); two v_exp_f32 (one per kernel);
-#        about 9.5 other vector instructions (dQ kernel: FMA, dP - D, times P,
-#        half a pack; dK/dV kernel: the same plus a second half pack and two
-#        accumulator-to-VGPR copies of S and dP).
+#        about 5.5 other vector instructions (dQ kernel: the FMA, the product
+#        P (dP - D) -- the dP accumulator starts from -D -- and half a pack;
+#        dK/dV kernel: the same plus a second half pack).
 KERNEL_WORK = {"fwd": {"mfma_flop_per_d": 4.0, "exp": 1.0, "valu": 4.0},
-               "bwd": {"mfma_flop_per_d": 14.0, "exp": 2.0, "valu": 9.5}}
+               "bwd": {"mfma_flop_per_d": 14.0, "exp": 2.0, "valu": 5.5}}
 
 
 def floors(pairs, d, pass_, rates):
