@@ -8,6 +8,9 @@
   what their generators write.
 * In each generated loop, no path has more than 15 LDS instructions in flight
   (lgkmcnt is a 4-bit counter), and every statement ends with none in flight.
+* No packed-fp32 vector instruction appears in the generated loops or the HIP
+  sources: the build compiles with packed fp32 disabled, and hand-written code
+  must not bring it back.
 """
 import os
 import re
@@ -98,3 +101,26 @@ def test_generated_loops_lds_counter():
                 mx, end = lds_in_flight(gen.generate(T, D))
                 assert mx <= 15, (gen.__name__, T, D, mx)
                 assert end == 0, (gen.__name__, T, D, end)
+
+
+def test_no_packed_fp32_instructions():
+    ops = ["v_pk_" + op + "_f32" for op in ("add", "mul", "fma")]
+    bad = []
+    for name, text in sources():
+        for op in ops:
+            if op in text:
+                bad.append((name, op))
+    sys.path.insert(0, CSRC)
+    try:
+        import gen_dkdv_loop
+        import gen_dq_loop
+        import gen_fwd_loop
+    finally:
+        sys.path.pop(0)
+    for gen in (gen_fwd_loop, gen_dq_loop, gen_dkdv_loop):
+        for T in ("BF16", "F16"):
+            for D in gen.HEAD_DIMS:
+                for line in gen.generate(T, D):
+                    if any(line.startswith(op) for op in ops):
+                        bad.append((gen.__name__, line))
+    assert not bad, bad
